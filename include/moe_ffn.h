@@ -1,0 +1,235 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) decode-step MoE feed-forward
+ * layer with a gated shared expert.
+ *
+ * The layer (per token x, all arithmetic fp32 on the GPU):
+ *   logits  l = Wr x                          (router, E rows)
+ *   ids     the k largest logits, ties to the lower expert index, rank order
+ *   weights w_j = softmax(l)[ids_j] / sum_j' softmax(l)[ids_j']
+ *   routed  r = sum_j w_j Wd[ids_j] (silu(Wg[ids_j] x) * (Wu[ids_j] x))
+ *   shared  S = Ws_d (silu(Ws_g x) * (Ws_u x)),  s = sigmoid(w_gate . x)
+ *   out     = r + s*S   (the product and the sum rounded separately)
+ * Structure: routed experts plus one gated shared expert, joined by a final
+ * add -- page "ggml-cuda: overlap the MoE shared expert on a separate stream",
+ * section "What this changes".  SwiGLU with separate gate and up matrices --
+ * page "ggml operator extensions", section "sd.cpp integration".
+ *
+ * Lifecycle (page "ggml operator extensions", section "Kernel selection": a
+ * prepare step that only plans and sizes workspace, an execute step that gets
+ * the stream, workspace and current addresses, and a destroy step):
+ *   moe_ffn_plan     host only: validates shapes, picks kernels, sizes ONE
+ *                    workspace; no HIP call, no device allocation, no launch.
+ *   moe_ffn_forward  enqueues the layer on the caller's stream and returns.
+ *   moe_ffn_destroy  releases the plan (NULL is a no-op).
+ *
+ * Ownership: the caller owns every tensor, the workspace and the stream; the
+ * library borrows them for the duration of the enqueued work (same page,
+ * section "Backend services": borrowed device and stream, ordered with the
+ * caller's work).  The plan owns a second HIP stream, two events and a
+ * 4 KiB device block of self-resetting routing counters, all created lazily
+ * by the first forward, which therefore must not run under stream capture.
+ *
+ * Threading: a plan serialises nothing.  Two forwards of one plan must not
+ * run concurrently (they share the counters and usually the workspace).
+ * Plans are independent of each other.
+ *
+ * Errors: every entry point validates before it enqueues anything and returns
+ * a specific status; it never retries and never switches to another algorithm
+ * on failure (same page, section "Kernel selection": errors propagate and a
+ * native path is never retried after launch).  moe_ffn_last_error() gives a
+ * human-readable reason for the last failure on the calling thread.  No C++
+ * exception crosses this ABI.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_ABI_VERSION 1
+
+typedef enum moe_ffn_status {
+    MOE_FFN_OK = 0,
+    MOE_FFN_ERR_INVALID_ARG = 1,          /* NULL where required, inconsistent shapes, unknown enum */
+    MOE_FFN_ERR_UNSUPPORTED = 2,          /* valid but outside the limits below, or first forward under capture */
+    MOE_FFN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below what the plan reported */
+    MOE_FFN_ERR_MISALIGNED = 4,           /* a tensor not 16-byte aligned, or the workspace not 256-byte aligned */
+    MOE_FFN_ERR_ALIAS = 5,                /* out overlaps an input other than by exact equality with x */
+    MOE_FFN_ERR_TOO_MANY_TOKENS = 6,      /* n_tokens < 0 or > desc.max_tokens */
+    MOE_FFN_ERR_HIP = 7,                  /* a HIP runtime call or kernel launch failed */
+    MOE_FFN_ERR_WRONG_DEVICE = 8          /* current device or stream's device differs from desc.device */
+} moe_ffn_status;
+
+typedef enum moe_ffn_dtype {
+    MOE_FFN_F32 = 0,
+    MOE_FFN_BF16 = 1,
+    /* 4-bit symmetric blocks: 32 consecutive elements along a row's reduction
+     * dimension form a block; element c of the row is in byte c/2, low nibble
+     * for even c, high nibble for odd c, stored as u = q + 8 (q in [-8, 7]);
+     * its value is scale[row][c/32] * q with one fp16 scale per block in a
+     * separate tensor. */
+    MOE_FFN_Q4_B32 = 2
+} moe_ffn_dtype;
+
+/* desc.flags ---------------------------------------------------------------
+ * Where the shared expert runs (page "ggml-cuda: overlap the MoE shared
+ * expert on a separate stream", section "What this changes": the shared
+ * expert forked onto one auxiliary stream and joined at the add, only in the
+ * small-batch mat-vec regime, output identical to sequential order).  Every
+ * mode gives bit-identical output for the same inputs. */
+#define MOE_FFN_SHARED_AUTO 0x0u   /* library choice per regime (see moe_ffn_plan_info) */
+#define MOE_FFN_SHARED_AUX 0x1u    /* second stream of the plan, event fork at entry, event join before the add */
+#define MOE_FFN_SHARED_SEQ 0x2u    /* same kernels, all on the caller's stream, shared branch first */
+#define MOE_FFN_SHARED_FUSED 0x3u  /* shared expert folded into the routed kernels' grids (fewest launches) */
+#define MOE_FFN_SHARED_MASK 0x3u
+/* Regime: mat-vec kernels while n_tokens <= desc.matvec_max_tokens, grouped
+ * MFMA GEMM above it.  The FORCE flags pin one regime for every n_tokens. */
+#define MOE_FFN_FORCE_MATVEC 0x10u
+#define MOE_FFN_FORCE_GEMM 0x20u
+/* Test hooks: a bounded (about 200 us) spin kernel at the head of the aux
+ * branch or of the main branch, to expose a missing wait or a launch on the
+ * wrong stream.  They change timing only, never results. */
+#define MOE_FFN_DEBUG_DELAY_AUX 0x100u
+#define MOE_FFN_DEBUG_DELAY_MAIN 0x200u
+
+/* Shapes and storage; frozen for the life of the plan.
+ * Limits (else MOE_FFN_ERR_UNSUPPORTED): hidden, inter, shared_inter
+ * multiples of 32 and at most 8192; n_experts 1..512; top_k 1..32 and
+ * <= n_experts; max_tokens 1..256; supported storage pairs (x_dtype,
+ * weight_dtype): (F32, F32), (BF16, BF16), (BF16, Q4_B32). */
+typedef struct moe_ffn_desc {
+    int32_t hidden;             /* H */
+    int32_t n_experts;          /* E */
+    int32_t top_k;              /* k */
+    int32_t inter;              /* I, routed-expert intermediate size */
+    int32_t shared_inter;       /* I_s, shared-expert intermediate size */
+    int32_t max_tokens;         /* largest n_tokens any forward of this plan may pass */
+    int32_t device;             /* HIP device ordinal the plan runs on */
+    int32_t x_dtype;            /* moe_ffn_dtype of x: F32 or BF16 */
+    int32_t weight_dtype;       /* moe_ffn_dtype of every routed and shared FFN matrix */
+    uint32_t flags;             /* MOE_FFN_SHARED_*, MOE_FFN_FORCE_*, MOE_FFN_DEBUG_* */
+    int32_t matvec_max_tokens;  /* regime switch; 0 = library default (16) */
+} moe_ffn_desc;
+
+/* Device pointers for one forward.  Row-major, contiguous, 16-byte aligned.
+ * Weights are in [out, in] orientation.  The router and the gate vector are
+ * always fp32.  For Q4_B32 storage a matrix of logical shape [.., R, K] is
+ * uint8 [.., R, K/2] plus an fp16 scale tensor [.., R, K/32]; the *_scale
+ * pointers must be NULL for other storage. */
+typedef struct moe_ffn_tensors {
+    const void *x;               /* [T, H] x_dtype */
+    const float *w_router;       /* [E, H] */
+    const void *w_gate;          /* [E, I, H] */
+    const void *w_up;            /* [E, I, H] */
+    const void *w_down;          /* [E, H, I] */
+    const uint16_t *w_gate_scale;  /* Q4_B32: fp16 [E, I, H/32] */
+    const uint16_t *w_up_scale;    /* Q4_B32: fp16 [E, I, H/32] */
+    const uint16_t *w_down_scale;  /* Q4_B32: fp16 [E, H, I/32] */
+    const void *sh_gate;         /* [I_s, H] */
+    const void *sh_up;           /* [I_s, H] */
+    const void *sh_down;         /* [H, I_s] */
+    const uint16_t *sh_gate_scale; /* Q4_B32: fp16 [I_s, H/32] */
+    const uint16_t *sh_up_scale;   /* Q4_B32: fp16 [I_s, H/32] */
+    const uint16_t *sh_down_scale; /* Q4_B32: fp16 [H, I_s/32] */
+    const float *gate_vec;       /* [H]: s = sigmoid(gate_vec . x) */
+    float *out;                  /* [T, H] fp32.  May equal x exactly (F32 x: in place);
+                                    any other overlap with an input -> MOE_FFN_ERR_ALIAS */
+    /* Optional outputs for tests (NULL = not written). */
+    int32_t *dbg_topk_ids;       /* [T, k] expert ids in rank order */
+    float *dbg_topk_weights;     /* [T, k] renormalised routing weights */
+    float *dbg_logits;           /* [T, E] router logits */
+    float *dbg_shared_gate;      /* [T] sigmoid gate of the shared expert */
+} moe_ffn_tensors;
+
+typedef struct moe_ffn_plan_s *moe_ffn_plan_t;
+
+/* What a plan decided (for tests, logs and the benchmark). */
+typedef struct moe_ffn_plan_info {
+    size_t workspace_bytes;      /* = shared_region + routing_region + phase_region */
+    size_t shared_region_bytes;  /* written only by the shared branch: disjoint from the rest */
+    size_t routing_region_bytes; /* routing results, live from the router to the join */
+    size_t phase_region_bytes;   /* max over the sequential steps of their scratch, not the sum */
+    int32_t matvec_max_tokens;   /* regime switch actually used */
+    uint32_t shared_mode_matvec; /* MOE_FFN_SHARED_{AUX,SEQ,FUSED} used in the mat-vec regime */
+    uint32_t shared_mode_gemm;   /* ... and in the grouped-GEMM regime */
+} moe_ffn_plan_info;
+
+/* Kernel ids for the profiling hooks. */
+typedef enum moe_ffn_kernel_id {
+    MOE_FFN_K_ROUTER = 0,       /* router GEMV + top-k + bucketing */
+    MOE_FFN_K_GATE_UP = 1,      /* mat-vec gate/up + SiLU*up (routed, or routed+shared when fused) */
+    MOE_FFN_K_DOWN = 2,         /* mat-vec down + weighted sum + join */
+    MOE_FFN_K_SH_GATE_UP = 3,   /* mat-vec gate/up of the shared expert alone */
+    MOE_FFN_K_SH_DOWN = 4,      /* mat-vec down of the shared expert alone */
+    MOE_FFN_K_GG_GATE_UP = 5,   /* grouped MFMA gate/up */
+    MOE_FFN_K_GG_DOWN = 6,      /* grouped MFMA down */
+    MOE_FFN_K_GG_JOIN = 7,      /* weighted sum + join after the grouped down */
+    MOE_FFN_K_COUNT = 8
+} moe_ffn_kernel_id;
+
+int32_t moe_ffn_abi_version(void);
+
+/* Static string for a status code ("unknown status" for other values). */
+const char *moe_ffn_status_string(int32_t status);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *moe_ffn_last_error(void);
+
+/* sizeof(moe_ffn_desc) for which = 0, sizeof(moe_ffn_tensors) for 1,
+ * sizeof(moe_ffn_plan_info) for 2, else 0 (lets bindings check their mirrors). */
+size_t moe_ffn_struct_size(int32_t which);
+
+/* Validates desc and creates a plan.  Host only: no HIP call.  On success
+ * *out_plan is the new plan and *workspace_bytes (if not NULL) the size of the
+ * one workspace every forward needs: the shared-branch region (disjoint,
+ * because it runs concurrently with the routed steps) plus the routing region
+ * plus the maximum, not the sum, of the sequential steps' scratch (page "ggml
+ * operator extensions", section "Kernel selection": workspace capacity is the
+ * maximum request, contents not preserved between calls).  On failure
+ * *out_plan is NULL. */
+moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
+                            size_t *workspace_bytes);
+
+/* Copies the plan's decisions into *info. */
+moe_ffn_status moe_ffn_plan_get_info(moe_ffn_plan_t plan, moe_ffn_plan_info *info);
+
+/* Enqueues the layer for tokens 0 .. n_tokens-1 on `stream` (a hipStream_t of
+ * desc.device; NULL is that device's null stream) and returns without
+ * waiting.  The workspace is device memory of at least the planned size,
+ * 256-byte aligned, owned by the caller; its contents are not preserved and
+ * every byte read is written earlier in the same call.  Private stream work
+ * rejoins `stream` before the call's last kernel, so later work on `stream`
+ * may reuse the workspace (same page and section: private-stream use must
+ * finish before later backend work can touch the workspace).  No host
+ * decision depends on tensor contents, so a forward can be captured into a
+ * HIP graph and replayed with new contents at the same addresses (page
+ * "ggml operator extensions", section "sd.cpp integration": capture-safe
+ * kernels, lazy setup in the first ordinary execution).  n_tokens == 0 is
+ * MOE_FFN_OK and enqueues nothing. */
+moe_ffn_status moe_ffn_forward(moe_ffn_plan_t plan, const moe_ffn_tensors *tensors,
+                               int32_t n_tokens, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Releases the plan, its stream, events and counters (waits for the plan's
+ * own stream to drain).  NULL is a no-op. */
+void moe_ffn_destroy(moe_ffn_plan_t plan);
+
+/* Profiling hooks for the benchmark.  While enabled, every later forward
+ * brackets each kernel launch with a pair of timing events on the stream that
+ * kernel runs on.  moe_ffn_profile_read waits for the recorded events, adds
+ * each kernel's total milliseconds and launch count into the caller's arrays
+ * of MOE_FFN_K_COUNT entries (overwriting them), and forgets the records. */
+moe_ffn_status moe_ffn_profile_enable(moe_ffn_plan_t plan, int32_t enable);
+moe_ffn_status moe_ffn_profile_read(moe_ffn_plan_t plan, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

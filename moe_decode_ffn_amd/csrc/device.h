@@ -1,0 +1,110 @@
+// device.h -- gfx950 device helpers shared by the MoE decode FFN kernels.
+//
+// Conventions (all kernels):
+//  * a weight row is read as 16-byte chunks; chunk c of a row is held by lane
+//    (c % LPR) of an LPR-lane segment, in register slot c / LPR, so one wave
+//    instruction reads LPR*16 contiguous bytes per segment (64 lanes = 1 KiB);
+//  * each lane accumulates its chunks in a fixed order, then the segment is
+//    reduced with DPP and cross-row shuffles; every lane of the segment ends
+//    with the same bits, so results never depend on which lane writes them;
+//  * no floating-point atomics anywhere: every sum has one fixed order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeffn {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+    _Float16 h = __builtin_bit_cast(_Float16, b);
+    return (float)h;
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on bf16 pairs, fp32 accumulate (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// ---- cross-lane ---------------------------------------------------------------
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (reverse within 8 lanes), row_mirror (reverse within 16).
+constexpr int kDppXor1 = 0xb1;
+constexpr int kDppXor2 = 0x4e;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned segments of LPR lanes (LPR in 8, 16, 32, 64); the result is
+// in every lane of the segment.  Each step adds a lane's value to its partner's
+// (a + b in one lane, b + a in the other), so all lanes hold identical bits.
+template <int LPR>
+__device__ __forceinline__ float seg_sum(float v) {
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment size");
+    v = v + dpp_f<kDppXor1>(v);
+    v = v + dpp_f<kDppXor2>(v);
+    v = v + dpp_f<kDppHalfMirror>(v);
+    if constexpr (LPR >= 16) v = v + dpp_f<kDppMirror>(v);
+    if constexpr (LPR >= 32) v = v + __shfl_xor(v, 16);
+    if constexpr (LPR >= 64) v = v + __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// ---- activation functions --------------------------------------------------------
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// ---- 16-byte chunk loads ---------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+// ---- 4-bit blocks ------------------------------------------------------------------
+// A chunk is one 32-element block: word i holds elements 8i..8i+7, element
+// 8i+n in bits 4n..4n+3 (low nibble = even element), stored as u = q + 8.
+// Nibbles become bf16 values 128 + u by placing them under the bf16 pattern
+// 0x43 (2^7): the byte-permute picks a nibble byte for the low half of each
+// bf16 and 0x43 for the high half.  Pairs come out as (e0,e2) (e4,e6) from
+// the low nibbles and (e1,e3) (e5,e7) from the high nibbles of a word.
+constexpr uint32_t kQ4Bias = 0x43434343u;
+constexpr uint32_t kSelLo = 0x04010400u;  // bytes 0 and 1 of the nibble word
+constexpr uint32_t kSelHi = 0x04030402u;  // bytes 2 and 3
+
+__device__ __forceinline__ void q4_word_to_bf16_pairs(uint32_t w, uint32_t out[4]) {
+    const uint32_t lo = w & 0x0f0f0f0fu;
+    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
+    out[0] = __builtin_amdgcn_perm(kQ4Bias, lo, kSelLo);  // (e0, e2)
+    out[1] = __builtin_amdgcn_perm(kQ4Bias, lo, kSelHi);  // (e4, e6)
+    out[2] = __builtin_amdgcn_perm(kQ4Bias, hi, kSelLo);  // (e1, e3)
+    out[3] = __builtin_amdgcn_perm(kQ4Bias, hi, kSelHi);  // (e5, e7)
+}
+
+// Rearranges 8 consecutive bf16 activations (4 words, element pairs (0,1)
+// (2,3) (4,5) (6,7)) into the pair order of q4_word_to_bf16_pairs.
+__device__ __forceinline__ void bf16x8_to_q4_order(const uint32_t x[4], uint32_t out[4]) {
+    out[0] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);  // (x0, x2)
+    out[1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);  // (x4, x6)
+    out[2] = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);  // (x1, x3)
+    out[3] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);  // (x5, x7)
+}
+
+}  // namespace moeffn

@@ -1,0 +1,339 @@
+// forward.cpp -- moe_ffn_forward / moe_ffn_destroy / profiling hooks.
+//
+// Order of work on the GPU for one forward (mat-vec regime):
+//   AUX   (the shared expert overlaps the routed chain; page "ggml-cuda: overlap
+//          the MoE shared expert on a separate stream", section "What this
+//          changes": one fork at the input, one join before the add)
+//            stream: record fork
+//            aux:    wait fork -> shared gate/up -> shared down (S) -> record join
+//            stream: router+top-k+bucketing -> routed gate/up -> wait join -> down+join
+//   SEQ   the same kernels, all on `stream`, shared branch first
+//   FUSED router+top-k+bucketing -> gate/up (routed + shared tiles in one grid)
+//          -> down (routed + shared rows, then the join) -- three launches
+// All three run identical per-element arithmetic, so their outputs are
+// bit-identical (the pages' requirement that the overlapped output equal the
+// sequential one).
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+using namespace moeffn;
+
+namespace {
+
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_ffn_status hip_fail(hipError_t e, const char *what) {
+    return set_error(MOE_FFN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hipEvent_t pool_event(moe_ffn_plan_s *P) {
+    if (!P->pool.empty()) {
+        hipEvent_t e = P->pool.back();
+        P->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs `launch` on stream s, bracketed by timing events when profiling.
+template <class F>
+hipError_t timed(moe_ffn_plan_s *P, int kernel, hipStream_t s, F &&launch) {
+    if (!P->profiling) return launch();
+    hipEvent_t a = pool_event(P), b = pool_event(P);
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, s);
+    P->prof.push_back({kernel, a, b});
+    return e;
+}
+
+moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return set_error(MOE_FFN_ERR_UNSUPPORTED,
+                         "the first forward of a plan creates its stream/events/counters and must not be captured");
+    if ((e = hipStreamCreateWithFlags(&P->aux, hipStreamNonBlocking)) != hipSuccess)
+        return hip_fail(e, "hipStreamCreateWithFlags");
+    if ((e = hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+    if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+    if ((e = hipMalloc(&P->counters, kCounterInts * sizeof(int))) != hipSuccess)
+        return hip_fail(e, "hipMalloc(counters)");
+    if ((e = hipMemsetAsync(P->counters, 0, kCounterInts * sizeof(int), stream)) != hipSuccess)
+        return hip_fail(e, "hipMemsetAsync(counters)");
+    P->ready = true;
+    return MOE_FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32_t n_tokens,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!P || !t) return set_error(MOE_FFN_ERR_INVALID_ARG, "plan and tensors must not be NULL");
+    const moe_ffn_desc &d = P->d;
+    if (n_tokens < 0 || n_tokens > d.max_tokens)
+        return set_error(MOE_FFN_ERR_TOO_MANY_TOKENS, "n_tokens must be in [0, max_tokens]");
+    if (n_tokens == 0) return MOE_FFN_OK;
+
+    const bool q4 = d.weight_dtype == MOE_FFN_Q4_B32;
+    const void *req[] = {t->x, t->w_router, t->w_gate, t->w_up, t->w_down, t->sh_gate,
+                         t->sh_up, t->sh_down, t->gate_vec, t->out};
+    for (const void *p : req)
+        if (!p) return set_error(MOE_FFN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    const void *sc[] = {t->w_gate_scale, t->w_up_scale, t->w_down_scale, t->sh_gate_scale,
+                        t->sh_up_scale, t->sh_down_scale};
+    for (const void *p : sc)
+        if ((p != nullptr) != q4)
+            return set_error(MOE_FFN_ERR_INVALID_ARG, "scale pointers must be set exactly for Q4_B32 storage");
+    if (!workspace) return set_error(MOE_FFN_ERR_INVALID_ARG, "workspace must not be NULL");
+    if (workspace_bytes < P->L.total)
+        return set_error(MOE_FFN_ERR_WORKSPACE_TOO_SMALL,
+                         "workspace needs " + std::to_string(P->L.total) + " bytes");
+    if (!aligned(workspace, kWsAlign)) return set_error(MOE_FFN_ERR_MISALIGNED, "workspace not 256-byte aligned");
+    const void *all[] = {t->x, t->w_router, t->w_gate, t->w_up, t->w_down, t->w_gate_scale,
+                         t->w_up_scale, t->w_down_scale, t->sh_gate, t->sh_up, t->sh_down,
+                         t->sh_gate_scale, t->sh_up_scale, t->sh_down_scale, t->gate_vec, t->out,
+                         t->dbg_topk_ids, t->dbg_topk_weights, t->dbg_logits, t->dbg_shared_gate};
+    for (const void *p : all)
+        if (!aligned(p, 16)) return set_error(MOE_FFN_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+
+    // aliasing: out may equal x exactly (same bytes, fp32 x), nothing else may overlap it
+    const size_t T = (size_t)n_tokens, H = d.hidden, E = d.n_experts, k = d.top_k;
+    const size_t I = d.inter, Is = d.shared_inter;
+    const size_t xb = d.x_dtype == MOE_FFN_F32 ? 4 : 2;
+    const int wk = P->wkind;
+    const Range out{t->out, T * H * 4};
+    const Range ins[] = {
+        {t->w_router, E * H * 4},
+        {t->w_gate, E * I * row_bytes_of(wk, (int)H)},
+        {t->w_up, E * I * row_bytes_of(wk, (int)H)},
+        {t->w_down, E * H * row_bytes_of(wk, (int)I)},
+        {t->w_gate_scale, q4 ? E * I * (H / 32) * 2 : 0},
+        {t->w_up_scale, q4 ? E * I * (H / 32) * 2 : 0},
+        {t->w_down_scale, q4 ? E * H * (I / 32) * 2 : 0},
+        {t->sh_gate, Is * row_bytes_of(wk, (int)H)},
+        {t->sh_up, Is * row_bytes_of(wk, (int)H)},
+        {t->sh_down, H * row_bytes_of(wk, (int)Is)},
+        {t->sh_gate_scale, q4 ? Is * (H / 32) * 2 : 0},
+        {t->sh_up_scale, q4 ? Is * (H / 32) * 2 : 0},
+        {t->sh_down_scale, q4 ? H * (Is / 32) * 2 : 0},
+        {t->gate_vec, H * 4},
+        {workspace, P->L.total},
+        {t->dbg_topk_ids, t->dbg_topk_ids ? T * k * 4 : 0},
+        {t->dbg_topk_weights, t->dbg_topk_weights ? T * k * 4 : 0},
+        {t->dbg_logits, t->dbg_logits ? T * E * 4 : 0},
+        {t->dbg_shared_gate, t->dbg_shared_gate ? T * 4 : 0},
+    };
+    for (const Range &r : ins)
+        if (overlap(out, r)) return set_error(MOE_FFN_ERR_ALIAS, "out overlaps an input, the workspace or a debug output");
+    const Range xr{t->x, T * H * xb};
+    if (overlap(out, xr) && !(t->out == t->x && xb == 4))
+        return set_error(MOE_FFN_ERR_ALIAS, "out may alias x only exactly (fp32 x)");
+    const Range ws{workspace, P->L.total};
+    if (overlap(xr, ws)) return set_error(MOE_FFN_ERR_ALIAS, "x overlaps the workspace");
+
+    // device checks
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != d.device) return set_error(MOE_FFN_ERR_WRONG_DEVICE, "current device differs from desc.device");
+    if (stream) {
+        hipDevice_t sd = -1;
+        if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if (sd != d.device) return set_error(MOE_FFN_ERR_WRONG_DEVICE, "stream belongs to another device");
+    }
+    if (!P->ready) {
+        moe_ffn_status st = lazy_init(P, stream);
+        if (st != MOE_FFN_OK) return st;
+    }
+
+    // workspace views
+    uint8_t *W = (uint8_t *)workspace;
+    const Layout &L = P->L;
+    float *sh_h = (float *)(W + L.sh_h), *sh_S = (float *)(W + L.sh_S);
+    float *gate_s = (float *)(W + L.gate_s), *wts = (float *)(W + L.wts);
+    int *ids = (int *)(W + L.ids), *n_unique = (int *)(W + L.n_unique);
+    int *pairs = (int *)(W + L.pairs), *pos_expert = (int *)(W + L.pos_expert);
+    int4 *slots = (int4 *)(W + L.slots);
+    float *logits = (float *)(W + L.logits), *h = (float *)(W + L.h);
+
+    const uint32_t mode = P->mode_matvec;
+    const int Ti = n_tokens;
+
+    // router + top-k + bucketing
+    RouterParams rp{};
+    rp.x = t->x;
+    rp.x_bf16 = d.x_dtype == MOE_FFN_BF16;
+    rp.T = Ti; rp.H = (int)H; rp.E = (int)E; rp.k = (int)k;
+    rp.router = t->w_router; rp.gate_vec = t->gate_vec;
+    rp.logits = logits; rp.ids = ids; rp.wts = wts; rp.gate_s = gate_s;
+    rp.slots = slots; rp.n_unique = n_unique; rp.pairs = pairs; rp.pos_expert = pos_expert;
+    rp.counters = P->counters;
+    rp.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
+    rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
+    rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
+    const int r_rows = router_rows_per_wg(P->map_router);
+    const int r_grid = (int)((E + 1 + r_rows - 1) / r_rows);
+    const int r_tiles = (Ti + rp.tok_tile - 1) / rp.tok_tile;
+
+    // gate/up
+    const size_t gu_rb = row_bytes_of(wk, (int)H);
+    GateUpParams gp{};
+    gp.x = t->x; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
+    gp.tok_per_pass = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
+    gp.wg = (const uint8_t *)t->w_gate; gp.wu = (const uint8_t *)t->w_up;
+    gp.sg = t->w_gate_scale; gp.su = t->w_up_scale; gp.I = (int)I;
+    gp.slots = slots; gp.n_unique = n_unique; gp.pairs = pairs; gp.h = h;
+    gp.swg = (const uint8_t *)t->sh_gate; gp.swu = (const uint8_t *)t->sh_up;
+    gp.ssg = t->sh_gate_scale; gp.ssu = t->sh_up_scale; gp.Is = (int)Is; gp.hs = sh_h;
+    const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
+    const int tiles_r = (int)((I + gu_rows - 1) / gu_rows);
+    const int tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
+    const int max_slots = (int)std::min(E, T * k);
+    const size_t gu_lds = (size_t)gp.tok_per_pass * H * xb;
+    (void)gu_rb;
+
+    // down
+    DownParams dp{};
+    dp.T = Ti; dp.H = (int)H; dp.k = (int)k; dp.E = (int)E;
+    dp.wd = (const uint8_t *)t->w_down; dp.sd = t->w_down_scale; dp.I = (int)I;
+    dp.h = h; dp.pairs = pairs; dp.pos_expert = pos_expert;
+    dp.swd = (const uint8_t *)t->sh_down; dp.ssd = t->sh_down_scale; dp.Is = (int)Is; dp.hs = sh_h;
+    dp.wts = wts; dp.gate_s = gate_s; dp.S_in = sh_S; dp.S_out = sh_S; dp.out = t->out;
+    const int d_rows = down_rows_per_wg(wk, P->map_down);
+    const int d_grid = (int)((H + d_rows - 1) / d_rows);
+
+    const bool delay_main = d.flags & MOE_FFN_DEBUG_DELAY_MAIN;
+    const bool delay_aux = d.flags & MOE_FFN_DEBUG_DELAY_AUX;
+    const uint64_t delay_ticks = 20000;  // 200 us of the 100 MHz constant clock
+
+    auto run_router = [&](hipStream_t s) {
+        return timed(P, MOE_FFN_K_ROUTER, s,
+                     [&] { return launch_router(rp, P->map_router, r_grid, r_tiles, s); });
+    };
+    auto run_gate_up = [&](hipStream_t s, bool routed, bool shared) {
+        GateUpParams g = gp;
+        g.routed_slots = routed ? max_slots : 0;
+        g.tiles_routed = tiles_r;
+        g.tiles_shared = shared ? tiles_s : 0;
+        const int grid = g.tiles_shared + g.routed_slots * g.tiles_routed;
+        const int kid = routed ? MOE_FFN_K_GATE_UP : MOE_FFN_K_SH_GATE_UP;
+        return timed(P, kid, s, [&] { return launch_gate_up(g, wk, P->map_gu, gu_rows, grid, gu_lds, s); });
+    };
+    auto run_down = [&](hipStream_t s, int dmode) {
+        DownParams q = dp;
+        q.mode = dmode;
+        q.n_routed = dmode == DOWN_SHARED_ONLY ? 0 : Ti * (int)k;
+        q.n_shared = dmode == DOWN_JOIN ? 0 : Ti;
+        const int kid = dmode == DOWN_SHARED_ONLY ? MOE_FFN_K_SH_DOWN : MOE_FFN_K_DOWN;
+        return timed(P, kid, s, [&] {
+            return launch_down(q, wk, P->map_down, d_rows, d_grid, 0, s);
+        });
+    };
+
+    hipError_t err = hipSuccess;
+    auto chk = [&](hipError_t x) {
+        if (err == hipSuccess && x != hipSuccess) err = x;
+    };
+    if (mode == MOE_FFN_SHARED_AUX) {
+        chk(hipEventRecord(P->ev_fork, stream));
+        chk(hipStreamWaitEvent(P->aux, P->ev_fork, 0));
+        if (delay_aux) chk(launch_delay(P->aux, delay_ticks));
+        chk(run_gate_up(P->aux, false, true));
+        chk(run_down(P->aux, DOWN_SHARED_ONLY));
+        chk(hipEventRecord(P->ev_join, P->aux));
+        if (delay_main) chk(launch_delay(stream, delay_ticks));
+        chk(run_router(stream));
+        chk(run_gate_up(stream, true, false));
+        chk(hipStreamWaitEvent(stream, P->ev_join, 0));
+        chk(run_down(stream, DOWN_JOIN));
+    } else if (mode == MOE_FFN_SHARED_SEQ) {
+        if (delay_aux) chk(launch_delay(stream, delay_ticks));
+        chk(run_gate_up(stream, false, true));
+        chk(run_down(stream, DOWN_SHARED_ONLY));
+        if (delay_main) chk(launch_delay(stream, delay_ticks));
+        chk(run_router(stream));
+        chk(run_gate_up(stream, true, false));
+        chk(run_down(stream, DOWN_JOIN));
+    } else {  // FUSED
+        if (delay_main || delay_aux) chk(launch_delay(stream, delay_ticks));
+        chk(run_router(stream));
+        chk(run_gate_up(stream, true, true));
+        chk(run_down(stream, DOWN_FUSED));
+    }
+    if (err != hipSuccess) return hip_fail(err, "kernel launch");
+    if ((err = hipGetLastError()) != hipSuccess) return hip_fail(err, "kernel launch");
+    return MOE_FFN_OK;
+}
+
+void moe_ffn_destroy(moe_ffn_plan_t P) {
+    if (!P) return;
+    if (P->aux) hipStreamSynchronize(P->aux);
+    for (auto &r : P->prof) {
+        hipEventSynchronize(r.stop);
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    for (hipEvent_t e : P->pool) hipEventDestroy(e);
+    if (P->counters) {
+        hipDeviceSynchronize();
+        hipFree(P->counters);
+    }
+    if (P->ev_fork) hipEventDestroy(P->ev_fork);
+    if (P->ev_join) hipEventDestroy(P->ev_join);
+    if (P->aux) hipStreamDestroy(P->aux);
+    delete P;
+}
+
+moe_ffn_status moe_ffn_profile_enable(moe_ffn_plan_t P, int32_t enable) {
+    if (!P) return set_error(MOE_FFN_ERR_INVALID_ARG, "plan must not be NULL");
+    P->profiling = enable != 0;
+    return MOE_FFN_OK;
+}
+
+moe_ffn_status moe_ffn_profile_read(moe_ffn_plan_t P, double *total_ms, int64_t *launches) {
+    if (!P || !total_ms || !launches) return set_error(MOE_FFN_ERR_INVALID_ARG, "NULL argument");
+    for (int i = 0; i < MOE_FFN_K_COUNT; ++i) {
+        total_ms[i] = 0.0;
+        launches[i] = 0;
+    }
+    moe_ffn_status st = MOE_FFN_OK;
+    for (auto &r : P->prof) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess && st == MOE_FFN_OK) st = hip_fail(e, "hipEventElapsedTime");
+        total_ms[r.kernel] += ms;
+        launches[r.kernel] += 1;
+        P->pool.push_back(r.start);
+        P->pool.push_back(r.stop);
+    }
+    P->prof.clear();
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// internal.h -- host-side structures shared by the planner, the launcher and
+// the kernel files of the MoE decode FFN library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "moe_ffn.h"
+
+namespace moeffn {
+
+constexpr int kMaxTokens = 256;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxDim = 8192;
+constexpr int kDefaultMatvecMax = 16;
+constexpr size_t kWsAlign = 256;
+constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
+constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
+constexpr int kCounterInts = 1024;        // 4 KiB of router tickets
+
+// weight storage as the kernels see it
+enum WKind : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
+
+// How a 16-byte-chunked row maps onto a wave: LPR lanes per row, NC chunks
+// per lane (chunk c of a row is read by lane c % LPR of the row's segment).
+struct RowMap {
+    int lpr = 64;
+    int nc = 1;
+    int n_chunks = 0;  // 16-byte chunks in one row
+};
+
+// Workspace layout: byte offsets from the workspace base, kWsAlign-aligned.
+struct Layout {
+    // shared-branch region (written only by the shared branch)
+    size_t sh_h = 0;    // f32 [Tmax][Is]
+    size_t sh_S = 0;    // f32 [Tmax][H]
+    size_t shared_bytes = 0;
+    // routing region (router -> join)
+    size_t gate_s = 0;     // f32 [Tmax]
+    size_t ids = 0;        // i32 [Tmax*k]
+    size_t wts = 0;        // f32 [Tmax*k]
+    size_t slots = 0;      // int4 [E]: (expert, first position, count, 0) per used expert
+    size_t n_unique = 0;   // i32 [4]
+    size_t pairs = 0;      // i32 [Tmax*k]: pair id t*k+j in expert-bucketed order
+    size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
+    size_t routing_bytes = 0;
+    // phase region: reused by the sequential steps
+    size_t logits = 0;  // router step: f32 [Tmax][E+1] (column E = shared-gate logit)
+    size_t h = 0;       // mat-vec gate/up -> down: f32 [Tmax*k][I]
+    size_t hb = 0;      // grouped GEMM gate/up -> down: bf16 [Tmax*k][I]
+    size_t y = 0;       // grouped GEMM down -> join: f32 [Tmax*k][H]
+    size_t phase_bytes = 0;
+    size_t total = 0;
+};
+
+struct ProfRec {
+    int kernel;
+    hipEvent_t start, stop;
+};
+
+}  // namespace moeffn
+
+struct moe_ffn_plan_s {
+    moe_ffn_desc d{};
+    moeffn::Layout L{};
+    int matvec_max = 0;
+    uint32_t mode_matvec = MOE_FFN_SHARED_FUSED;
+    uint32_t mode_gemm = MOE_FFN_SHARED_SEQ;
+    int wkind = 0;
+    // row maps: router rows (fp32, K=H), gate/up rows (K=H), down rows (K=max(I,Is))
+    moeffn::RowMap map_router, map_gu, map_down;
+    // lazily created device state
+    bool ready = false;
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    int *counters = nullptr;
+    // profiling
+    bool profiling = false;
+    std::vector<moeffn::ProfRec> prof;
+    std::vector<hipEvent_t> pool;
+};
+
+namespace moeffn {
+
+// ---- kernel launch parameter blocks ---------------------------------------
+
+struct RouterParams {
+    const void *x;
+    int x_bf16;
+    int T, H, E, k;
+    const float *router;    // [E][H]
+    const float *gate_vec;  // [H] (acts as row E)
+    float *logits;          // [T][E+1]
+    int *ids;               // [T*k]
+    float *wts;             // [T*k]
+    float *gate_s;          // [T]
+    int4 *slots;            // [E]
+    int *n_unique;          // [1]
+    int *pairs;             // [T*k]
+    int *pos_expert;        // [T*k]
+    int *counters;          // [n_tok_tiles + 1], zero between calls
+    int tok_tile;           // tokens per workgroup column
+    int32_t *dbg_ids;
+    float *dbg_w, *dbg_logits, *dbg_gate;
+};
+
+struct GateUpParams {
+    const void *x;
+    int T, H, k, E;
+    int tok_per_pass;  // tokens staged in LDS per pass
+    // routed experts
+    const uint8_t *wg, *wu;        // [E][I] rows
+    const uint16_t *sg, *su;       // Q4 scales [E][I][H/32]
+    int I;
+    const int4 *slots;
+    const int *n_unique;
+    const int *pairs;
+    float *h;                      // [T*k][I]
+    int routed_slots;              // expert slots in the grid
+    int tiles_routed;              // workgroup tiles per routed expert
+    // shared expert
+    const uint8_t *swg, *swu;
+    const uint16_t *ssg, *ssu;
+    int Is;
+    float *hs;                     // [T][Is]
+    int tiles_shared;              // 0 = shared expert not in this launch
+};
+
+enum DownMode : int { DOWN_FUSED = 0, DOWN_JOIN = 1, DOWN_SHARED_ONLY = 2 };
+
+struct DownParams {
+    int T, H, k, E;
+    int pos_per_pass;  // activation vectors staged in LDS per pass (set by the launcher)
+    int mode;
+    // routed experts
+    const uint8_t *wd;   // [E][H] rows of I
+    const uint16_t *sd;  // [E][H][I/32]
+    int I;
+    const float *h;      // [T*k][I]
+    const int *pairs;
+    const int *pos_expert;
+    int n_routed;        // routed positions in this launch (T*k or 0)
+    // shared expert
+    const uint8_t *swd;  // [H] rows of Is
+    const uint16_t *ssd; // [H][Is/32]
+    int Is;
+    const float *hs;     // [T][Is]
+    int n_shared;        // shared positions in this launch (T or 0)
+    // join
+    const float *wts;    // [T*k]
+    const float *gate_s; // [T]
+    const float *S_in;   // [T][H] (DOWN_JOIN)
+    float *S_out;        // [T][H] (DOWN_SHARED_ONLY)
+    float *out;          // [T][H]
+};
+
+// ---- launchers (kernel files) -------------------------------------------
+hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
+                         hipStream_t s);
+hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int rows_per_wg,
+                          int grid, size_t lds, hipStream_t s);
+hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int rows_per_wg, int grid,
+                       size_t lds, hipStream_t s);
+hipError_t launch_delay(hipStream_t s, uint64_t ticks);
+
+// rows each workgroup covers for a kernel family and row map
+int router_rows_per_wg(const RowMap &m);
+int gate_up_rows_per_wg(int wkind, const RowMap &m);
+int down_rows_per_wg(int wkind, const RowMap &m);
+// LDS of the down kernel for n_pos positions; sets the positions staged per pass
+size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int n_pos, int *pos_per_pass);
+
+// ---- planner helpers (plan.cpp) ---------------------------------------------
+RowMap make_row_map(size_t row_bytes);
+size_t row_bytes_of(int wkind, int k_elems);
+moe_ffn_status set_error(moe_ffn_status st, const std::string &msg);
+
+}  // namespace moeffn

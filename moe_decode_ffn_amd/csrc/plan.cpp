@@ -1,0 +1,178 @@
+// plan.cpp -- host-only planning for the MoE decode FFN layer: validation,
+// kernel geometry and the workspace layout.  No HIP runtime call is made here
+// (planning may run before any device work exists: page "ggml operator
+// extensions", section "Kernel selection", the prepare step).
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace moeffn {
+
+static thread_local std::string g_last_error;
+
+moe_ffn_status set_error(moe_ffn_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+size_t row_bytes_of(int wkind, int k_elems) {
+    switch (wkind) {
+    case W_F32: return (size_t)k_elems * 4;
+    case W_BF16: return (size_t)k_elems * 2;
+    default: return (size_t)k_elems / 2;  // W_Q4 (scales live in their own tensor)
+    }
+}
+
+static int pow2_ceil(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+RowMap make_row_map(size_t row_bytes) {
+    RowMap m;
+    m.n_chunks = (int)(row_bytes / 16);
+    if (m.n_chunks >= 64) {
+        m.lpr = 64;
+        m.nc = pow2_ceil((m.n_chunks + 63) / 64);
+    } else {
+        m.lpr = std::max(8, pow2_ceil(m.n_chunks));
+        m.nc = 1;
+    }
+    return m;
+}
+
+static size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+}  // namespace moeffn
+
+using namespace moeffn;
+
+extern "C" {
+
+int32_t moe_ffn_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char *moe_ffn_last_error(void) { return g_last_error.c_str(); }
+
+const char *moe_ffn_status_string(int32_t status) {
+    switch (status) {
+    case MOE_FFN_OK: return "ok";
+    case MOE_FFN_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_FFN_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_FFN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_FFN_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_FFN_ERR_ALIAS: return "output overlaps an input";
+    case MOE_FFN_ERR_TOO_MANY_TOKENS: return "token count out of range";
+    case MOE_FFN_ERR_HIP: return "HIP runtime error";
+    case MOE_FFN_ERR_WRONG_DEVICE: return "wrong device";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_ffn_struct_size(int32_t which) {
+    switch (which) {
+    case 0: return sizeof(moe_ffn_desc);
+    case 1: return sizeof(moe_ffn_tensors);
+    case 2: return sizeof(moe_ffn_plan_info);
+    default: return 0;
+    }
+}
+
+moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
+                            size_t *workspace_bytes) {
+    if (out_plan) *out_plan = nullptr;
+    if (!desc || !out_plan) return set_error(MOE_FFN_ERR_INVALID_ARG, "desc and out_plan must not be NULL");
+    const moe_ffn_desc d = *desc;
+    const uint32_t known = MOE_FFN_SHARED_MASK | MOE_FFN_FORCE_MATVEC | MOE_FFN_FORCE_GEMM |
+                           MOE_FFN_DEBUG_DELAY_AUX | MOE_FFN_DEBUG_DELAY_MAIN;
+    if (d.flags & ~known) return set_error(MOE_FFN_ERR_INVALID_ARG, "unknown flag bits");
+    if ((d.flags & MOE_FFN_FORCE_MATVEC) && (d.flags & MOE_FFN_FORCE_GEMM))
+        return set_error(MOE_FFN_ERR_INVALID_ARG, "FORCE_MATVEC and FORCE_GEMM are exclusive");
+    if (d.hidden <= 0 || d.n_experts <= 0 || d.top_k <= 0 || d.inter <= 0 || d.shared_inter <= 0 ||
+        d.max_tokens <= 0 || d.device < 0 || d.matvec_max_tokens < 0)
+        return set_error(MOE_FFN_ERR_INVALID_ARG, "sizes must be positive (device, matvec_max_tokens >= 0)");
+    if (d.top_k > d.n_experts) return set_error(MOE_FFN_ERR_INVALID_ARG, "top_k > n_experts");
+    if (d.x_dtype < MOE_FFN_F32 || d.x_dtype > MOE_FFN_BF16 || d.weight_dtype < MOE_FFN_F32 ||
+        d.weight_dtype > MOE_FFN_Q4_B32)
+        return set_error(MOE_FFN_ERR_INVALID_ARG, "unknown dtype");
+    for (int v : {d.hidden, d.inter, d.shared_inter})
+        if (v % 32 != 0 || v > kMaxDim)
+            return set_error(MOE_FFN_ERR_UNSUPPORTED, "hidden/inter/shared_inter must be multiples of 32, at most 8192");
+    if (d.n_experts > kMaxExperts) return set_error(MOE_FFN_ERR_UNSUPPORTED, "n_experts > 512");
+    if (d.top_k > kMaxTopK) return set_error(MOE_FFN_ERR_UNSUPPORTED, "top_k > 32");
+    if (d.max_tokens > kMaxTokens) return set_error(MOE_FFN_ERR_UNSUPPORTED, "max_tokens > 256");
+    const bool pair_ok = (d.x_dtype == MOE_FFN_F32 && d.weight_dtype == MOE_FFN_F32) ||
+                         (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_BF16) ||
+                         (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_Q4_B32);
+    if (!pair_ok) return set_error(MOE_FFN_ERR_UNSUPPORTED, "unsupported (x_dtype, weight_dtype) pair");
+    if (d.flags & MOE_FFN_FORCE_GEMM)
+        return set_error(MOE_FFN_ERR_UNSUPPORTED, "grouped-GEMM regime is not available in this build");
+
+    moe_ffn_plan_s *P = new (std::nothrow) moe_ffn_plan_s;
+    if (!P) return set_error(MOE_FFN_ERR_INVALID_ARG, "out of host memory");
+    P->d = d;
+    P->wkind = d.weight_dtype;
+    P->matvec_max = d.max_tokens;  // only the mat-vec regime exists in this build
+    const uint32_t mode = d.flags & MOE_FFN_SHARED_MASK;
+    P->mode_matvec = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_AUX : mode;
+    P->mode_gemm = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_SEQ : mode;
+
+    const int H = d.hidden, E = d.n_experts, k = d.top_k, I = d.inter, Is = d.shared_inter;
+    const size_t T = (size_t)d.max_tokens, P_ = T * k;
+    P->map_router = make_row_map(row_bytes_of(W_F32, H));
+    P->map_gu = make_row_map(row_bytes_of(P->wkind, H));
+    P->map_down = make_row_map(row_bytes_of(P->wkind, std::max(I, Is)));
+
+    // LDS of the down kernel: activation staging + per-pair results of its rows
+    const int Tmv = P->matvec_max;
+    const size_t lds_down = down_lds_bytes(P->wkind, P->map_down, I, Is, Tmv * k + Tmv, nullptr);
+    const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
+    if (!maps_ok || lds_down > kLdsLimit) {
+        delete P;
+        return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
+    }
+
+    Layout &L = P->L;
+    size_t c = 0;
+    L.sh_h = c;       c += align_up(T * Is * 4);
+    L.sh_S = c;       c += align_up(T * H * 4);
+    L.shared_bytes = c;
+    L.gate_s = c;     c += align_up(T * 4);
+    L.ids = c;        c += align_up(P_ * 4);
+    L.wts = c;        c += align_up(P_ * 4);
+    L.slots = c;      c += align_up((size_t)E * 16);
+    L.n_unique = c;   c += align_up(16);
+    L.pairs = c;      c += align_up(P_ * 4);
+    L.pos_expert = c; c += align_up(P_ * 4);
+    L.routing_bytes = c - L.shared_bytes;
+    const size_t base = c;
+    const size_t ph_router = align_up(T * (E + 1) * 4);
+    const size_t ph_matvec = align_up(P_ * I * 4);
+    L.logits = base;
+    L.h = base;
+    L.hb = base;
+    L.y = base;
+    L.phase_bytes = std::max(ph_router, ph_matvec);
+    L.total = base + L.phase_bytes;
+
+    *out_plan = P;
+    if (workspace_bytes) *workspace_bytes = L.total;
+    return MOE_FFN_OK;
+}
+
+moe_ffn_status moe_ffn_plan_get_info(moe_ffn_plan_t plan, moe_ffn_plan_info *info) {
+    if (!plan || !info) return set_error(MOE_FFN_ERR_INVALID_ARG, "plan and info must not be NULL");
+    info->workspace_bytes = plan->L.total;
+    info->shared_region_bytes = plan->L.shared_bytes;
+    info->routing_region_bytes = plan->L.routing_bytes;
+    info->phase_region_bytes = plan->L.phase_bytes;
+    info->matvec_max_tokens = plan->matvec_max;
+    info->shared_mode_matvec = plan->mode_matvec;
+    info->shared_mode_gemm = plan->mode_gemm;
+    return MOE_FFN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP layer, called through the C ABI, against the CPU oracle.
+
+Small layers span several workgroup tiles, token passes, router token tiles
+and partially covered 16-byte chunk slots; the decode layer (hidden 2048,
+256 experts, top-8, inter 512) runs at its real size for batch 1, 8, 128 in
+bf16 and batch 1, 4 in 4-bit blocks.  Every shared-expert mode (aux stream,
+sequential, fused) must match the oracle and each other bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from moe_decode_ffn_amd import ffn, synth
+from tests.gpu_common import compare, device, oracle_threads, run_gpu, tol_for
+from tests.helpers import oracle_layer, oracle_tokens
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"aux": ffn.SHARED_AUX, "seq": ffn.SHARED_SEQ, "fused": ffn.SHARED_FUSED}
+
+SMALL = {
+    # name: (shape, seed, token counts)
+    "tiny_fp32": (synth.TINY, 0, (1, 3)),
+    "bf16_ragged_chunks": (synth.LayerShape(160, 12, 3, 96, 64, "bf16", "bf16"), 5, (1, 5, 17)),
+    "q4_ragged": (synth.LayerShape(192, 10, 3, 96, 160, "bf16", "q4"), 6, (1, 4, 9)),
+    "fp32_two_slots": (synth.LayerShape(288, 20, 4, 64, 96, "f32", "f32"), 7, (2, 11)),
+    "bf16_big_buckets": (synth.LayerShape(96, 4, 2, 64, 32, "bf16", "bf16"), 8, (40,)),
+    "bf16_k_equals_e": (synth.LayerShape(64, 4, 4, 32, 32, "bf16", "bf16"), 9, (3,)),
+    "bf16_one_expert": (synth.LayerShape(96, 1, 1, 64, 32, "bf16", "bf16"), 10, (2,)),
+    "q4_wide": (synth.LayerShape(1024, 16, 4, 256, 128, "bf16", "q4"), 11, (1, 6)),
+}
+
+
+def _plan(shape, max_tokens, mode, extra=0):
+    return ffn.MoeFfn.for_shape(shape, max_tokens=max_tokens, flags=MODES[mode] | extra)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_layers_all_modes(orc, name):
+    dev = device()
+    shape, seed, counts = SMALL[name]
+    layer = synth.make_layer(shape, seed)
+    dl = synth.layer_to(layer, dev)
+    plans = {m: _plan(shape, max(counts), m) for m in MODES}
+    for T in counts:
+        x = synth.make_tokens(shape, T, seed, stream=T)
+        ref = orc.forward(oracle_layer(layer), oracle_tokens(x))
+        outs = {}
+        for m, mf in plans.items():
+            print(f"[small] {name} T={T} mode={m}", flush=True)
+            got = run_gpu(mf, dl, x.to(dev))
+            compare(orc, layer, x, got, tol_for(shape), ref=ref)
+            outs[m] = got["out"]
+        assert torch.equal(outs["aux"], outs["seq"]), "aux vs sequential must be bit-identical"
+        assert torch.equal(outs["aux"], outs["fused"]), "aux vs fused must be bit-identical"
+
+
+# ---- the decode layer at full size ----------------------------------------------------
+
+_LAYERS: dict = {}
+
+
+def _decode_layer(shape, seed):
+    """Drawn on the device with torch's seeded generator, copied to the host for the oracle."""
+    key = (shape, seed)
+    if key not in _LAYERS:
+        dev = device()
+        dl = synth.make_layer_device(shape, seed, dev)
+        _LAYERS.clear()
+        _LAYERS[key] = (dl, {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dl.items()})
+    return _LAYERS[key]
+
+
+FULL = {
+    "decode_bf16_t1": (synth.DECODE_BF16, 1, 1),
+    "decode_bf16_t8": (synth.DECODE_BF16, 2, 8),
+    "decode_q4_t1": (synth.DECODE_Q4, 3, 1),
+    "decode_q4_t4": (synth.DECODE_Q4, 3, 4),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_decode_layer_full_size(orc, name):
+    dev = device()
+    shape, seed, T = FULL[name]
+    dl, lc = _decode_layer(shape, seed)
+    x = synth.make_tokens(shape, T, seed, stream=T)
+    ref = orc.forward(oracle_layer(lc), oracle_tokens(x), nthreads=oracle_threads())
+    outs = {}
+    for m in MODES:
+        print(f"[full] {name} mode={m}", flush=True)
+        mf = _plan(shape, T, m)
+        got = run_gpu(mf, dl, x.to(dev))
+        rep = compare(orc, lc, x, got, tol_for(shape), ref=ref)
+        print(f"  {rep}", flush=True)
+        outs[m] = got["out"]
+        mf.close()
+    assert torch.equal(outs["aux"], outs["seq"])
+    assert torch.equal(outs["aux"], outs["fused"])
+
+
+def test_decode_bf16_t128(orc):
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 4, 128
+    dl, lc = _decode_layer(shape, seed)
+    x = synth.make_tokens(shape, T, seed, stream=T)
+    print("[full] decode_bf16_t128", flush=True)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
+    got = run_gpu(mf, dl, x.to(dev))
+    rep = compare(orc, lc, x, got, tol_for(shape))
+    print(f"  {rep}", flush=True)
+    assert rep["unique_experts"] > 200
+
+
+# ---- determinism, races, streams, capture ---------------------------------------------
+
+def test_run_to_run_and_poisoned_workspace():
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 2, 8
+    dl, _ = _decode_layer(shape, seed)
+    x = synth.make_tokens(shape, T, seed, stream=T).to(dev)
+    for m in MODES:
+        mf = _plan(shape, T, m)
+        ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+        first = run_gpu(mf, dl, x, ws=ws, poison=0)["out"]
+        for i, pat in enumerate((0xFF, 0x7F, 0xA5, 0x00) * 5):
+            again = run_gpu(mf, dl, x, ws=ws, poison=pat)["out"]
+            assert torch.equal(first, again), f"mode {m}: run {i} with workspace fill {pat:#x} differs"
+        mf.close()
+
+
+@pytest.mark.parametrize("hook", ["delay_aux", "delay_main"])
+def test_stream_order_with_injected_delay(hook):
+    """A spin at the head of one branch must not change a single bit."""
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 2, 8
+    dl, _ = _decode_layer(shape, seed)
+    x = synth.make_tokens(shape, T, seed, stream=T).to(dev)
+    base = run_gpu(_plan(shape, T, "seq"), dl, x)["out"]
+    flag = ffn.DEBUG_DELAY_AUX if hook == "delay_aux" else ffn.DEBUG_DELAY_MAIN
+    mf = _plan(shape, T, "aux", flag)
+    for _ in range(3):
+        assert torch.equal(run_gpu(mf, dl, x)["out"], base)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_graph_capture_and_replay(mode):
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 2, 8
+    dl, _ = _decode_layer(shape, seed)
+    mf = _plan(shape, T, mode)
+    ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+    x_static = synth.make_tokens(shape, T, seed, stream=100).to(dev)
+    out_static = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    mf.forward(dl, x_static, out_static, ws)  # first call: lazy set-up, never captured
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mf.forward(dl, x_static, out_static, ws)
+    for i in range(4):
+        xi = synth.make_tokens(shape, T, seed, stream=200 + i).to(dev)
+        eager_out = torch.empty_like(out_static)
+        eager_ws = torch.empty_like(ws)
+        mf.forward(dl, xi, eager_out, eager_ws)
+        torch.cuda.synchronize()
+        x_static.copy_(xi)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, eager_out), f"replay {i} differs from eager"
+
+
+# ---- edge cases ----------------------------------------------------------------------
+
+def test_in_place_fp32(orc):
+    dev = device()
+    shape = synth.TINY
+    layer = synth.make_layer(shape, 0)
+    dl = synth.layer_to(layer, dev)
+    x = synth.make_tokens(shape, 3, 0, stream=3)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=3)
+    ref = run_gpu(mf, dl, x.to(dev))["out"]
+    buf = x.to(dev).clone()
+    ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+    mf.forward(dl, buf, buf, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.cpu(), ref)
+
+
+def test_zero_tokens_is_a_no_op():
+    dev = device()
+    shape = synth.TINY
+    dl = synth.layer_to(synth.make_layer(shape, 0), dev)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=4)
+    x = torch.zeros(0, shape.hidden, dtype=torch.float32, device=dev)
+    out = torch.full((1, shape.hidden), 7.0, device=dev)
+    ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+    mf.forward(dl, x, out, ws, n_tokens=0)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_max_tokens_256(orc):
+    dev = device()
+    shape = synth.LayerShape(128, 16, 2, 256, 64, "bf16", "bf16")
+    layer = synth.make_layer(shape, 12)
+    x = synth.make_tokens(shape, 256, 12)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=256)
+    got = run_gpu(mf, synth.layer_to(layer, dev), x.to(dev))
+    compare(orc, layer, x, got, tol_for(shape))
+
+
+def test_power_of_two_homogeneity():
+    dev = device()
+    shape = synth.LayerShape(256, 16, 4, 128, 96, "bf16", "bf16")
+    layer = synth.make_layer(shape, 13)
+    x = synth.make_tokens(shape, 5, 13).to(dev)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=5)
+    base = run_gpu(mf, synth.layer_to(layer, dev), x)["out"]
+    doubled = dict(layer)
+    doubled["down"] = (layer["down"].float() * 2).to(torch.bfloat16)
+    doubled["sh_down"] = (layer["sh_down"].float() * 2).to(torch.bfloat16)
+    got = run_gpu(mf, synth.layer_to(doubled, dev), x)["out"]
+    assert torch.equal(got, base * 2)
+
+
+def test_q4_matches_dequantised_fp32():
+    """The in-register 4-bit path against the fp32 path on exactly dequantised weights."""
+    dev = device()
+    shape = synth.LayerShape(512, 12, 3, 128, 96, "bf16", "q4")
+    layer = synth.make_layer(shape, 14)
+    x = synth.make_tokens(shape, 4, 14)
+    q = run_gpu(ffn.MoeFfn.for_shape(shape, max_tokens=4), synth.layer_to(layer, dev), x.to(dev))
+
+    def deq(name):
+        w, s = layer[name], layer[name + "_scale"]
+        lo = (w & 15).to(torch.float32) - 8
+        hi = (w >> 4).to(torch.float32) - 8
+        qv = torch.stack((lo, hi), dim=-1).flatten(-2)
+        return qv * s.to(torch.float32).repeat_interleave(32, dim=-1)
+
+    fshape = shape.with_(x_dtype="f32", w_dtype="f32")
+    fl = {"shape": fshape, "router": layer["router"], "gate_vec": layer["gate_vec"]}
+    for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        fl[n] = deq(n).contiguous()
+        fl[n + "_scale"] = None
+    f = run_gpu(ffn.MoeFfn.for_shape(fshape, max_tokens=4), synth.layer_to(fl, dev),
+                x.to(torch.float32).to(dev))
+    assert torch.equal(q["ids"], f["ids"])
+    scale = f["out"].abs().max()
+    assert (q["out"] - f["out"]).abs().max() <= 1e-4 * scale
+
+
+def test_expert_permutation_equivariance():
+    dev = device()
+    shape = synth.LayerShape(256, 16, 4, 128, 64, "bf16", "q4")
+    layer = synth.make_layer(shape, 15)
+    x = synth.make_tokens(shape, 6, 15).to(dev)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=6)
+    a = run_gpu(mf, synth.layer_to(layer, dev), x)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(shape.n_experts))
+    pl = dict(layer)
+    pl["router"] = layer["router"][perm].contiguous()
+    for n in ("gate", "up", "down", "gate_scale", "up_scale", "down_scale"):
+        pl[n] = layer[n][perm].contiguous()
+    b = run_gpu(mf, synth.layer_to(pl, dev), x)
+    assert torch.equal(perm[b["ids"].long()].to(torch.int32), a["ids"])
+    assert (a["out"] - b["out"]).abs().max() <= 1e-5 * a["out"].abs().max()
