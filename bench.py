@@ -1,0 +1,242 @@
+"""Benchmark: MoE decode FFN layer tokens/s and expert-weight HBM bandwidth on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16_t1]
+                    [--mode auto|aux|seq|fused] [--eager] [--no-cpu-baseline]
+
+A step is one forward of the whole layer (router, top-k, bucketing, routed
+gate/up, down, shared expert, join) over one batch of tokens.  The timed steps
+cycle through L distinct device-resident copies of the layer and a pool of
+token batches, so consecutive uses of a copy are hundreds of MB apart and the
+256 MB Infinity Cache cannot serve them.  Steps are launched as HIP graphs of
+a rotation window (the decode loop is graph-replayed) unless --eager.
+
+Prints one JSON line.  `value` is tokens/s; the expert-weight bytes a step
+must read are the routed experts actually selected (counted from the kernels'
+own routing output in an untimed pass) plus the shared expert.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer decode tokens/s at batch 1/8 + expert-weight HBM GB/s vs peak"
+LAYER_COPIES = {"bf16": 16, "q4": 32, "f32": 16}
+TOKEN_POOL = 8
+WINDOW_REPEATS = 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_decode_ffn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def expert_bytes(shape) -> tuple[int, int]:
+    """(gate+up bytes, down bytes) of one expert (or the shared expert) in its storage."""
+    H, I = shape.hidden, shape.inter
+    if shape.w_dtype == "q4":
+        per = lambda rows, k: rows * (k // 2) + rows * (k // 32) * 2  # noqa: E731
+    else:
+        b = 2 if shape.w_dtype == "bf16" else 4
+        per = lambda rows, k: rows * k * b  # noqa: E731
+    return 2 * per(I, H), per(H, I)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20000)
+    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--workload", default="decode_bf16_t1")
+    ap.add_argument("--mode", default="auto", choices=["auto", "aux", "seq", "fused"])
+    ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic", default=None, help="traffic JSON written from rocprofv3 counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU split of the layer is a "
+              "design (see DESIGN.md), not a measured path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from moe_decode_ffn_amd import ffn, synth
+
+    if args.workload not in synth.WORKLOADS:
+        print(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        return 2
+    shape, seed, counts = synth.WORKLOADS[args.workload]
+    T = counts[-1]
+    dev = torch.device("cuda:0")
+    mode = {"auto": ffn.SHARED_AUTO, "aux": ffn.SHARED_AUX, "seq": ffn.SHARED_SEQ,
+            "fused": ffn.SHARED_FUSED}[args.mode]
+
+    # ---- inputs resident in HBM -----------------------------------------------------
+    L = LAYER_COPIES[shape.w_dtype] if shape.hidden >= 1024 else 2
+    layers = [synth.make_layer_device(shape, 100 + i, dev) for i in range(L)]
+    xs = [synth.make_tokens_device(shape, T, 1000 + j, dev) for j in range(TOKEN_POOL)]
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=mode)
+    info = mf.info()
+    ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    window = [(i % L, i % TOKEN_POOL) for i in range(L * WINDOW_REPEATS)]
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    structs = {(li, xi): ffn.MoeFfn.tensors(layers[li], xs[xi], out) for li, xi in set(window)}
+
+    def launch(step: int, h: int = handle) -> None:
+        key = window[step % len(window)]
+        ffn.moe_ffn_forward(mf.plan, structs[key], T, ws.data_ptr(), mf.workspace_bytes, h)
+
+    # ---- untimed pass: routing of every (copy, tokens) pair of the window ---------------
+    launch(0)  # lazy set-up (stream, events, counters) outside any capture
+    torch.cuda.synchronize()
+    ids = torch.empty(T, shape.top_k, dtype=torch.int32, device=dev)
+    uniq = []
+    for li, xi in window:
+        mf.forward(layers[li], xs[xi], out, ws, dbg={"ids": ids})
+        uniq.append(len(torch.unique(ids)))
+    torch.cuda.synchronize()
+    unique_mean = float(np.mean(uniq))
+    gu_b, d_b = expert_bytes(shape)
+    bytes_per_step = unique_mean * (gu_b + d_b) + (gu_b + d_b)  # routed + shared expert weights
+
+    # ---- graphs of whole rotation windows ----------------------------------------------------
+    graphs = {}
+
+    def graph_for(n: int):
+        if n not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                h = torch.cuda.current_stream().cuda_stream  # the capture stream
+                for s in range(n):
+                    launch(s, h)
+            graphs[n] = g
+        return graphs[n]
+
+    def run_steps(k: int) -> None:
+        if args.eager:
+            for s in range(k):
+                launch(s)
+            return
+        full, rest = divmod(k, len(window))
+        if full:
+            g = graph_for(len(window))
+            for _ in range(full):
+                g.replay()
+        if rest:
+            graph_for(rest).replay()
+
+    if not args.eager:
+        graph_for(len(window))
+        if args.steps % len(window):
+            graph_for(args.steps % len(window))
+        torch.cuda.synchronize()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+    gbps = bytes_per_step * args.steps / elapsed / 1e9
+
+    # ---- per-kernel durations from HIP events on each kernel's own stream -------------------
+    prof_steps = min(args.steps, 4 * len(window))
+    mf.profile_enable(True)
+    for s in range(prof_steps):
+        launch(s)
+    torch.cuda.synchronize()
+    prof = mf.profile_read()
+    mf.profile_enable(False)
+    shared_mode = {1: "aux", 2: "seq", 3: "fused"}[info.shared_mode_matvec]
+    dominant = "gate_up"
+    ms_tot, n_launch = prof[dominant]
+    avg_us = ms_tot * 1e3 / max(1, n_launch)
+    gu_units = unique_mean + (1 if shared_mode == "fused" else 0)
+    achieved = gu_units * gu_b / (avg_us * 1e-6) / 1e9
+    kernels = {k: round(v[0] * 1e3 / v[1], 3) for k, v in prof.items() if v[1]}
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        rec = json.load(open(args.traffic))
+        if rec.get("kernel_source_hash") == kernel_source_hash() and rec.get("workload") == args.workload:
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    # ---- the oracle on the host cores (a bounded sample of the same workload) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.oracle import Oracle
+        from tests.helpers import oracle_layer, oracle_tokens
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        orc = Oracle()
+        host_layer = oracle_layer({k: (v.cpu() if isinstance(v, torch.Tensor) else v)
+                                   for k, v in layers[0].items()})
+        calls, c0 = 0, time.perf_counter()
+        while True:
+            orc.forward(host_layer, oracle_tokens(xs[calls % TOKEN_POOL].cpu()), nthreads=cores)
+            calls += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        c_el = time.perf_counter() - c0
+        cpu = {"value": round(T * calls / c_el, 3), "unit": "tokens/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{calls} forwards of {T} token(s) on layer copy 0 ({c_el:.1f} s, fp64, "
+                         f"{cores} OpenMP threads over rows)"}
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "q4": "q4_b32+bf16", "f32": "f32"}[shape.w_dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "hidden": shape.hidden, "experts": shape.n_experts,
+                   "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
+                   "tokens": T, "weights": shape.w_dtype, "accumulate": "fp32",
+                   "layer_copies": L, "shared_mode": shared_mode,
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "expert_weight_GBps": round(gbps, 1),
+        "expert_weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "unique_experts_per_step": round(unique_mean, 3),
+        "expert_weight_bytes_per_step": int(bytes_per_step),
+        "kernel_avg_us": kernels,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_us": round(avg_us, 3),
+                     "algorithmic_bytes_per_launch": int(gu_units * gu_b)},
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(res))
+    mf.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

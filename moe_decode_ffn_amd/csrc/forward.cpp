@@ -194,6 +194,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.slots = slots; rp.n_unique = n_unique; rp.pairs = pairs; rp.pos_expert = pos_expert;
     rp.counters = P->counters;
     rp.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
+    // small batches: the routed gate/up workgroups rank the batch themselves
+    const bool route_in_gu = Ti <= kRouteInGateUpMaxT;
+    rp.route = route_in_gu ? 0 : 1;
     rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
     rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
     const int r_rows = router_rows_per_wg(P->map_router);
@@ -207,14 +210,18 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gp.tok_per_pass = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
     gp.wg = (const uint8_t *)t->w_gate; gp.wu = (const uint8_t *)t->w_up;
     gp.sg = t->w_gate_scale; gp.su = t->w_up_scale; gp.I = (int)I;
-    gp.slots = slots; gp.n_unique = n_unique; gp.pairs = pairs; gp.h = h;
+    gp.route_here = route_in_gu ? 1 : 0;
+    gp.logits = logits; gp.ids = ids; gp.wts = wts; gp.gate_s = gate_s;
+    gp.slots = slots; gp.n_unique = n_unique; gp.pairs = pairs; gp.pos_expert = pos_expert;
+    gp.dbg_ids = t->dbg_topk_ids; gp.dbg_w = t->dbg_topk_weights;
+    gp.dbg_logits = t->dbg_logits; gp.dbg_gate = t->dbg_shared_gate;
+    gp.h = h;
     gp.swg = (const uint8_t *)t->sh_gate; gp.swu = (const uint8_t *)t->sh_up;
     gp.ssg = t->sh_gate_scale; gp.ssu = t->sh_up_scale; gp.Is = (int)Is; gp.hs = sh_h;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
     const int tiles_r = (int)((I + gu_rows - 1) / gu_rows);
     const int tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
     const int max_slots = (int)std::min(E, T * k);
-    const size_t gu_lds = (size_t)gp.tok_per_pass * H * xb;
     (void)gu_rb;
 
     // down
@@ -242,7 +249,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         g.tiles_shared = shared ? tiles_s : 0;
         const int grid = g.tiles_shared + g.routed_slots * g.tiles_routed;
         const int kid = routed ? MOE_FFN_K_GATE_UP : MOE_FFN_K_SH_GATE_UP;
-        return timed(P, kid, s, [&] { return launch_gate_up(g, wk, P->map_gu, gu_rows, grid, gu_lds, s); });
+        return timed(P, kid, s, [&] { return launch_gate_up(g, wk, P->map_gu, gu_rows, grid, 0, s); });
     };
     auto run_down = [&](hipStream_t s, int dmode) {
         DownParams q = dp;

@@ -48,9 +48,9 @@ struct Layout {
     size_t n_unique = 0;   // i32 [4]
     size_t pairs = 0;      // i32 [Tmax*k]: pair id t*k+j in expert-bucketed order
     size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
+    size_t logits = 0;     // f32 [Tmax][E+1] (column E = shared-gate logit), router -> gate/up
     size_t routing_bytes = 0;
     // phase region: reused by the sequential steps
-    size_t logits = 0;  // router step: f32 [Tmax][E+1] (column E = shared-gate logit)
     size_t h = 0;       // mat-vec gate/up -> down: f32 [Tmax*k][I]
     size_t hb = 0;      // grouped GEMM gate/up -> down: bf16 [Tmax*k][I]
     size_t y = 0;       // grouped GEMM down -> join: f32 [Tmax*k][H]
@@ -105,6 +105,7 @@ struct RouterParams {
     int *pos_expert;        // [T*k]
     int *counters;          // [n_tok_tiles + 1], zero between calls
     int tok_tile;           // tokens per workgroup column
+    int route;              // 1: rank and bucket in this launch (ticket path)
     int32_t *dbg_ids;
     float *dbg_w, *dbg_logits, *dbg_gate;
 };
@@ -117,9 +118,19 @@ struct GateUpParams {
     const uint8_t *wg, *wu;        // [E][I] rows
     const uint16_t *sg, *su;       // Q4 scales [E][I][H/32]
     int I;
-    const int4 *slots;
-    const int *n_unique;
-    const int *pairs;
+    // routing: read (route_here = 0) or computed by every routed workgroup from
+    // the logits and published by the first one (route_here = 1)
+    int route_here;
+    const float *logits;           // [T][E+1]
+    int *ids;                      // [T*k]
+    float *wts;                    // [T*k]
+    float *gate_s;                 // [T]
+    int4 *slots;
+    int *n_unique;
+    int *pairs;
+    int *pos_expert;
+    int32_t *dbg_ids;
+    float *dbg_w, *dbg_logits, *dbg_gate;
     float *h;                      // [T*k][I]
     int routed_slots;              // expert slots in the grid
     int tiles_routed;              // workgroup tiles per routed expert
@@ -173,7 +184,13 @@ int router_rows_per_wg(const RowMap &m);
 int gate_up_rows_per_wg(int wkind, const RowMap &m);
 int down_rows_per_wg(int wkind, const RowMap &m);
 // LDS of the down kernel for n_pos positions; sets the positions staged per pass
-size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int n_pos, int *pos_per_pass);
+size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int T, int k, int n_routed,
+                      int n_shared, int *pos_per_pass);
+// LDS of the gate/up kernel (staging + in-kernel routing when route_here)
+size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);
+size_t router_lds_bytes(const RouterParams &p);
+// largest batch whose routing the gate/up workgroups compute themselves
+constexpr int kRouteInGateUpMaxT = 16;
 
 // ---- planner helpers (plan.cpp) ---------------------------------------------
 RowMap make_row_map(size_t row_bytes);

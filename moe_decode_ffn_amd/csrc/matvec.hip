@@ -17,6 +17,7 @@
 // block, dequantised in registers).
 #include "device.h"
 #include "internal.h"
+#include "routing.h"
 
 namespace moeffn {
 
@@ -117,10 +118,11 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPR, sl = lane % LPR;
-    const int H = p.H;
+    const int H = p.H, T = p.T, k = p.k, E = p.E;
     const size_t rb = WK == W_F32 ? (size_t)H * 4 : WK == W_BF16 ? (size_t)H * 2 : (size_t)H / 2;
     const int n_chunks = (int)(rb / 16);
     const int nsb = H / 32;  // 4-bit blocks per row
+    const int n_pairs = T * k;
 
     // which expert and tile
     int b = blockIdx.x;
@@ -128,22 +130,64 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     const uint16_t *Sg = nullptr, *Su = nullptr;
     int n_rows, tile, ntok, start = 0, hstride;
     float *hout;
+    const int *pairs = p.pairs;
     bool routed;
     if (b < p.tiles_shared) {
         routed = false;
         Wg = p.swg; Wu = p.swu; Sg = p.ssg; Su = p.ssu;
-        n_rows = p.Is; tile = b; ntok = p.T; hout = p.hs; hstride = p.Is;
+        n_rows = p.Is; tile = b; ntok = T; hout = p.hs; hstride = p.Is;
     } else {
         routed = true;
         b -= p.tiles_shared;
         const int slot = b / p.tiles_routed;
         tile = b - slot * p.tiles_routed;
-        if (slot >= *p.n_unique) return;
-        const int4 s = p.slots[slot];
+        int4 s;
+        if (p.route_here) {
+            // rank every token of the batch (one wave per token), bucket in LDS
+            uint8_t *ra = lds + (size_t)p.tok_per_pass * H * XB;
+            int *r_ids = reinterpret_cast<int *>(ra);
+            float *r_w = reinterpret_cast<float *>(r_ids + n_pairs);
+            float *r_gate = r_w + n_pairs;
+            int *r_pairs = reinterpret_cast<int *>(r_gate + T);
+            int *r_pose = r_pairs + n_pairs;
+            int *r_nu = r_pose + n_pairs;
+            int4 *r_slots = reinterpret_cast<int4 *>(ra + (((size_t)(4 * n_pairs + T + 4) * 4 + 15) & ~(size_t)15));
+            uint32_t *scratch = reinterpret_cast<uint32_t *>(r_slots + (E < n_pairs ? E : n_pairs));
+            const bool publish = b == 0;  // the first routed workgroup writes the tables
+            for (int t = wave; t < T; t += kWaves) {
+                RouteOut o{r_ids + t * k, r_w + t * k, r_gate + t,
+                           publish && p.dbg_ids ? p.dbg_ids + t * k : nullptr,
+                           publish && p.dbg_w ? p.dbg_w + t * k : nullptr,
+                           publish && p.dbg_gate ? p.dbg_gate + t : nullptr,
+                           publish && p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
+                route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
+            }
+            __syncthreads();
+            bucket_pairs(r_ids, T, k, E, scratch, r_slots, r_pairs, r_pose, r_nu);
+            __syncthreads();
+            const int nu = *r_nu;
+            if (publish) {
+                for (int i = tid; i < n_pairs; i += 256) {
+                    p.ids[i] = r_ids[i];
+                    p.wts[i] = r_w[i];
+                    p.pairs[i] = r_pairs[i];
+                    p.pos_expert[i] = r_pose[i];
+                }
+                for (int i = tid; i < T; i += 256) p.gate_s[i] = r_gate[i];
+                for (int i = tid; i < nu; i += 256) p.slots[i] = r_slots[i];
+                if (tid == 0) *p.n_unique = nu;
+            }
+            if (slot >= nu) return;
+            s = r_slots[slot];
+            pairs = r_pairs;
+        } else {
+            if (slot >= *p.n_unique) return;
+            s = p.slots[slot];
+        }
         const int e = s.x;
         start = s.y;
         ntok = s.z;
-        if (e < 0 || e >= p.E || start < 0 || ntok <= 0 || start + ntok > p.T * p.k) return;
+        if (e < 0 || e >= E || start < 0 || ntok <= 0 || start + ntok > n_pairs) return;
         const size_t r0 = (size_t)e * p.I;
         Wg = p.wg + r0 * rb;
         Wu = p.wu + r0 * rb;
@@ -178,13 +222,12 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     for (int t0 = 0; t0 < ntok; t0 += p.tok_per_pass) {
         const int nt = min(p.tok_per_pass, ntok - t0);
         __syncthreads();
-        const int n_pairs = p.T * p.k;
         for (int i = tid; i < nt * xrow16; i += 256) {
             const int a = i / xrow16, c = i - a * xrow16;
             int tok = t0 + a;
             if (routed) {
-                const int pr = p.pairs[start + t0 + a];
-                tok = (pr >= 0 && pr < n_pairs) ? pr / p.k : 0;
+                const int pr = pairs[start + t0 + a];
+                tok = (pr >= 0 && pr < n_pairs) ? pr / k : 0;
             }
             reinterpret_cast<uint4 *>(lds)[i] =
                 ld16((const uint8_t *)p.x + ((size_t)tok * xrow16 + c) * 16);
@@ -235,8 +278,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                     }
                 }
             }
-            const int orow = routed ? p.pairs[start + t0 + a] : t0 + a;
-            const bool ook = orow >= 0 && orow < (routed ? n_pairs : p.T);
+            const int orow = routed ? pairs[start + t0 + a] : t0 + a;
+            const bool ook = orow >= 0 && orow < (routed ? n_pairs : T);
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const float gs = seg_sum<LPR>(g[i]);
@@ -248,6 +291,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
 }
 
 // ---- down + weighted sum + join -----------------------------------------------------------
+// LDS: act[PP][Kmax] | ybuf[n_pos][RPWG] | pair id and expert per routed position |
+//      weights [T*k] | gate [T] | S [T][RPWG] (join mode)
 template <int WK, int LPR, int NC>
 __global__ __launch_bounds__(256) void k_down(DownParams p) {
     constexpr int RPI = 64 / LPR;
@@ -260,13 +305,36 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
     const int H = p.H, k = p.k, T = p.T;
     const int Kmax = p.I > p.Is ? p.I : p.Is;
     const int PP = p.pos_per_pass;                     // <= QB, set by the launcher
+    const int n_pos = p.n_routed + p.n_shared;
+    const int NPR = T * k;
     float *act = reinterpret_cast<float *>(lds);       // [PP][Kmax]
-    float *ybuf = act + (size_t)PP * Kmax;             // [n_routed + n_shared][RPWG]
+    float *ybuf = act + (size_t)PP * Kmax;             // [n_pos][RPWG]
+    int *t_pair = reinterpret_cast<int *>(ybuf + (size_t)n_pos * RPWG);  // [n_routed]
+    int *t_exp = t_pair + p.n_routed;                  // [n_routed]
+    float *t_w = reinterpret_cast<float *>(t_exp + p.n_routed);  // [T*k]
+    float *t_g = t_w + NPR;                            // [T]
+    float *t_S = t_g + T;                              // [T][RPWG]
     const int row0 = blockIdx.x * RPWG;
     const int r = row0 + wave * RPI + seg;
     const bool rv = r < H;
     const int rl = r - row0;
-    const int n_pos = p.n_routed + p.n_shared;
+
+    // tables of this launch, all loads in flight together
+    for (int i = tid; i < p.n_routed; i += 256) {
+        const int pr = p.pairs[i], e = p.pos_expert[i];
+        t_pair[i] = (pr >= 0 && pr < NPR) ? pr : 0;
+        t_exp[i] = (e >= 0 && e < p.E) ? e : -1;
+    }
+    if (p.mode != DOWN_SHARED_ONLY) {
+        for (int i = tid; i < NPR; i += 256) t_w[i] = p.wts[i];
+        for (int i = tid; i < T; i += 256) t_g[i] = p.gate_s[i];
+        if (p.mode == DOWN_JOIN)
+            for (int i = tid; i < T * RPWG; i += 256) {
+                const int t = i / RPWG, c = i - t * RPWG;
+                t_S[i] = row0 + c < H ? p.S_in[(size_t)t * H + row0 + c] : 0.f;
+            }
+    }
+    __syncthreads();
 
     for (int q0 = 0; q0 < n_pos; q0 += PP) {
         const int nq = min(PP, n_pos - q0);
@@ -281,8 +349,8 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
             int K = p.Is;
             bool ok = a < nq;
             if (ok && q < p.n_routed) {
-                const int e = p.pos_expert[q];
-                ok = e >= 0 && e < p.E;
+                const int e = t_exp[q];
+                ok = e >= 0;
                 K = p.I;
                 const size_t rbk = WK == W_F32 ? (size_t)K * 4 : WK == W_BF16 ? (size_t)K * 2 : (size_t)K / 2;
                 Wm = p.wd + (size_t)(ok ? e : 0) * H * rbk;
@@ -299,7 +367,7 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
                     sc[a][n] = okc ? f16_to_f32(Sm[(size_t)r * (K / 32) + c]) : 0.f;
             }
         }
-        __syncthreads();  // the previous pass is done with act[]
+        if (q0 > 0) __syncthreads();  // the previous pass is done with act[]
         const int k4 = Kmax / 4;
         for (int i = tid; i < nq * k4; i += 256) {
             const int a = i / k4, c4 = i - a * k4;
@@ -307,8 +375,7 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
             const float *src;
             int K;
             if (q < p.n_routed) {
-                const int pr = p.pairs[q];
-                src = p.h + (size_t)(pr >= 0 && pr < T * k ? pr : 0) * p.I;
+                src = p.h + (size_t)t_pair[q] * p.I;
                 K = p.I;
             } else {
                 src = p.hs + (size_t)(q - p.n_routed) * p.Is;
@@ -345,8 +412,8 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
                 }
                 acc = seg_sum<LPR>(acc);
                 const int q = q0 + a;
-                const int slot = q < p.n_routed ? p.pairs[q] : p.n_routed + (q - p.n_routed);
-                if (sl == 0 && rv && slot >= 0 && slot < n_pos) ybuf[(size_t)slot * RPWG + rl] = acc;
+                const int slot = q < p.n_routed ? t_pair[q] : q;
+                if (sl == 0 && rv) ybuf[(size_t)slot * RPWG + rl] = acc;
             }
         }
     }
@@ -360,13 +427,12 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
             p.S_out[(size_t)t * H + rr] = ybuf[(size_t)t * RPWG + c];
             continue;
         }
-        const float *wt = p.wts + (size_t)t * k;
+        const float *wt = t_w + (size_t)t * k;
         const float *yr = ybuf + (size_t)t * k * RPWG + c;
         float routed = wt[0] * yr[0];
         for (int j = 1; j < k; ++j) routed = fmaf(wt[j], yr[(size_t)j * RPWG], routed);
-        const float S = p.mode == DOWN_FUSED ? ybuf[(size_t)(p.n_routed + t) * RPWG + c]
-                                             : p.S_in[(size_t)t * H + rr];
-        p.out[(size_t)t * H + rr] = __fadd_rn(routed, __fmul_rn(p.gate_s[t], S));
+        const float S = p.mode == DOWN_FUSED ? ybuf[(size_t)(p.n_routed + t) * RPWG + c] : t_S[i];
+        p.out[(size_t)t * H + rr] = __fadd_rn(routed, __fmul_rn(t_g[t], S));
     }
 }
 
@@ -388,6 +454,8 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
                           int grid, size_t lds, hipStream_t s) {
     (void)rows_per_wg;
     if (grid <= 0) return hipSuccess;
+    lds = gate_up_lds_bytes(p, wkind == W_F32 ? 4 : 2);
+    if (lds > kLdsLimit) return hipErrorInvalidValue;
 #define GU_LAUNCH(L, N)                                                                          \
     if (wkind == W_F32) hipLaunchKernelGGL((k_gate_up<W_F32, L, N>), dim3(grid), dim3(256), lds, s, p); \
     else if (wkind == W_BF16) hipLaunchKernelGGL((k_gate_up<W_BF16, L, N>), dim3(grid), dim3(256), lds, s, p); \
@@ -397,13 +465,28 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
     return hipGetLastError();
 }
 
-size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int n_pos, int *pos_per_pass) {
+size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int T, int k, int n_routed,
+                      int n_shared, int *pos_per_pass) {
     const int qb = m.nc >= 16 ? 1 : 16 / m.nc;
     const int Kmax = I > Is ? I : Is;
     int pp = (int)(kStageBytes / ((size_t)Kmax * 4));
     pp = pp < 1 ? 1 : pp > qb ? qb : pp;
+    const int rpwg = down_rows_per_wg(wkind, m);
+    const size_t fixed = (size_t)(n_routed + n_shared) * rpwg + 2 * (size_t)n_routed + (size_t)T * k + T +
+                         (size_t)T * rpwg;
+    while (pp > 1 && (fixed + (size_t)pp * Kmax) * 4 > kLdsLimit) pp >>= 1;  // fewer staged vectors
     if (pos_per_pass) *pos_per_pass = pp;
-    return (size_t)pp * Kmax * 4 + (size_t)n_pos * down_rows_per_wg(wkind, m) * 4;
+    return (fixed + (size_t)pp * Kmax) * 4;
+}
+
+size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes) {
+    size_t b = (size_t)p.tok_per_pass * p.H * xbytes;
+    if (p.route_here) {
+        const int np = p.T * p.k;
+        b += (((size_t)(4 * np + p.T + 4) * 4 + 15) & ~(size_t)15) + (size_t)(p.E < np ? p.E : np) * 16 +
+             (size_t)bucket_scratch_ints(p.E, p.T) * 4;
+    }
+    return b;
 }
 
 hipError_t launch_down(const DownParams &p_in, int wkind, const RowMap &m, int rows_per_wg,
@@ -411,7 +494,7 @@ hipError_t launch_down(const DownParams &p_in, int wkind, const RowMap &m, int r
     (void)rows_per_wg;
     if (grid <= 0) return hipSuccess;
     DownParams p = p_in;
-    lds = down_lds_bytes(wkind, m, p.I, p.Is, p.n_routed + p.n_shared, &p.pos_per_pass);
+    lds = down_lds_bytes(wkind, m, p.I, p.Is, p.T, p.k, p.n_routed, p.n_shared, &p.pos_per_pass);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
 #define D_LAUNCH(L, N)                                                                           \
     if (wkind == W_F32) hipLaunchKernelGGL((k_down<W_F32, L, N>), dim3(grid), dim3(256), lds, s, p); \

@@ -126,11 +126,19 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     P->map_gu = make_row_map(row_bytes_of(P->wkind, H));
     P->map_down = make_row_map(row_bytes_of(P->wkind, std::max(I, Is)));
 
-    // LDS of the down kernel: activation staging + per-pair results of its rows
+    // LDS of each kernel at the largest batch it can see
     const int Tmv = P->matvec_max;
-    const size_t lds_down = down_lds_bytes(P->wkind, P->map_down, I, Is, Tmv * k + Tmv, nullptr);
+    const size_t lds_down = down_lds_bytes(P->wkind, P->map_down, I, Is, Tmv, k, Tmv * k, Tmv, nullptr);
+    GateUpParams gq{};
+    gq.T = std::min(Tmv, kRouteInGateUpMaxT); gq.H = H; gq.k = k; gq.E = E; gq.route_here = 1;
+    const int xbytes = d.x_dtype == MOE_FFN_F32 ? 4 : 2;
+    gq.tok_per_pass = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
+    RouterParams rq{};
+    rq.T = d.max_tokens; rq.H = H; rq.E = E; rq.k = k; rq.x_bf16 = xbytes == 2;
+    rq.tok_tile = gq.tok_per_pass; rq.route = 1;
     const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
-    if (!maps_ok || lds_down > kLdsLimit) {
+    if (!maps_ok || lds_down > kLdsLimit || gate_up_lds_bytes(gq, xbytes) > kLdsLimit ||
+        router_lds_bytes(rq) > kLdsLimit) {
         delete P;
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
     }
@@ -147,15 +155,16 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.n_unique = c;   c += align_up(16);
     L.pairs = c;      c += align_up(P_ * 4);
     L.pos_expert = c; c += align_up(P_ * 4);
+    // logits stay live through the gate/up step, whose workgroups rank the batch
+    // while others already write h, so they cannot share the phase region
+    L.logits = c;     c += align_up(T * (E + 1) * 4);
     L.routing_bytes = c - L.shared_bytes;
     const size_t base = c;
-    const size_t ph_router = align_up(T * (E + 1) * 4);
     const size_t ph_matvec = align_up(P_ * I * 4);
-    L.logits = base;
     L.h = base;
     L.hb = base;
     L.y = base;
-    L.phase_bytes = std::max(ph_router, ph_matvec);
+    L.phase_bytes = ph_matvec;
     L.total = base + L.phase_bytes;
 
     *out_plan = P;

@@ -119,13 +119,13 @@ def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
     shared = _align(T * Is * 4) + _align(T * H * 4)
+    # logits are read by the gate/up workgroups while others write h: routing region
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 16) + _align(16)
-               + 2 * _align(T * k * 4))
-    phases = {"router logits": _align(T * (E + 1) * 4), "mat-vec h": _align(T * k * I * 4)}
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4))
+    phases = {"mat-vec h": _align(T * k * I * 4)}
     assert info.shared_region_bytes == shared
     assert info.routing_region_bytes == routing
     assert info.phase_region_bytes == max(phases.values())
-    assert info.phase_region_bytes < sum(phases.values())
     assert ws == info.workspace_bytes == shared + routing + max(phases.values())
 
 

@@ -76,6 +76,11 @@ def _decode_layer(shape, seed):
 FULL = {
     "decode_bf16_t1": (synth.DECODE_BF16, 1, 1),
     "decode_bf16_t8": (synth.DECODE_BF16, 2, 8),
+    # around the largest batch whose routing the gate/up workgroups compute
+    # themselves (more workgroups than fit on the GPU at once from T = 4 on)
+    "decode_bf16_t4": (synth.DECODE_BF16, 2, 4),
+    "decode_bf16_t16": (synth.DECODE_BF16, 2, 16),
+    "decode_bf16_t17": (synth.DECODE_BF16, 2, 17),
     "decode_q4_t1": (synth.DECODE_Q4, 3, 1),
     "decode_q4_t4": (synth.DECODE_Q4, 3, 4),
 }
