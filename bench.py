@@ -166,7 +166,7 @@ def main() -> int:
     prof = mf.profile_read()
     mf.profile_enable(False)
     shared_mode = {1: "aux", 2: "seq", 3: "fused"}[info.shared_mode_matvec]
-    dominant = "gate_up"
+    dominant = "gate_up"  # the routed (+ shared when fused) gate/up launch moves the most bytes
     ms_tot, n_launch = prof[dominant]
     avg_us = ms_tot * 1e3 / max(1, n_launch)
     gu_units = unique_mean + (1 if shared_mode == "fused" else 0)

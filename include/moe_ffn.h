@@ -25,12 +25,12 @@
  * Ownership: the caller owns every tensor, the workspace and the stream; the
  * library borrows them for the duration of the enqueued work (same page,
  * section "Backend services": borrowed device and stream, ordered with the
- * caller's work).  The plan owns a second HIP stream, two events and a
- * 4 KiB device block of self-resetting routing counters, all created lazily
- * by the first forward, which therefore must not run under stream capture.
+ * caller's work).  The plan owns a second HIP stream and two events, created
+ * lazily by the first forward, which therefore must not run under stream
+ * capture.
  *
  * Threading: a plan serialises nothing.  Two forwards of one plan must not
- * run concurrently (they share the counters and usually the workspace).
+ * run concurrently (they share the plan's stream and usually the workspace).
  * Plans are independent of each other.
  *
  * Errors: every entry point validates before it enqueues anything and returns
@@ -83,7 +83,7 @@ typedef enum moe_ffn_dtype {
  * expert forked onto one auxiliary stream and joined at the add, only in the
  * small-batch mat-vec regime, output identical to sequential order).  Every
  * mode gives bit-identical output for the same inputs. */
-#define MOE_FFN_SHARED_AUTO 0x0u   /* library choice per regime (see moe_ffn_plan_info) */
+#define MOE_FFN_SHARED_AUTO 0x0u   /* FUSED up to matvec_max_tokens, AUX above (moe_ffn_plan_info) */
 #define MOE_FFN_SHARED_AUX 0x1u    /* second stream of the plan, event fork at entry, event join before the add */
 #define MOE_FFN_SHARED_SEQ 0x2u    /* same kernels, all on the caller's stream, shared branch first */
 #define MOE_FFN_SHARED_FUSED 0x3u  /* shared expert folded into the routed kernels' grids (fewest launches) */
@@ -155,22 +155,23 @@ typedef struct moe_ffn_plan_info {
     size_t shared_region_bytes;  /* written only by the shared branch: disjoint from the rest */
     size_t routing_region_bytes; /* routing results, live from the router to the join */
     size_t phase_region_bytes;   /* max over the sequential steps of their scratch, not the sum */
-    int32_t matvec_max_tokens;   /* regime switch actually used */
-    uint32_t shared_mode_matvec; /* MOE_FFN_SHARED_{AUX,SEQ,FUSED} used in the mat-vec regime */
-    uint32_t shared_mode_gemm;   /* ... and in the grouped-GEMM regime */
+    int32_t matvec_max_tokens;   /* small-batch threshold actually used */
+    uint32_t shared_mode_matvec; /* MOE_FFN_SHARED_{AUX,SEQ,FUSED} used for n_tokens <= threshold */
+    uint32_t shared_mode_gemm;   /* ... and above it */
 } moe_ffn_plan_info;
 
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
-    MOE_FFN_K_ROUTER = 0,       /* router GEMV + top-k + bucketing */
-    MOE_FFN_K_GATE_UP = 1,      /* mat-vec gate/up + SiLU*up (routed, or routed+shared when fused) */
-    MOE_FFN_K_DOWN = 2,         /* mat-vec down + weighted sum + join */
-    MOE_FFN_K_SH_GATE_UP = 3,   /* mat-vec gate/up of the shared expert alone */
-    MOE_FFN_K_SH_DOWN = 4,      /* mat-vec down of the shared expert alone */
-    MOE_FFN_K_GG_GATE_UP = 5,   /* grouped MFMA gate/up */
-    MOE_FFN_K_GG_DOWN = 6,      /* grouped MFMA down */
-    MOE_FFN_K_GG_JOIN = 7,      /* weighted sum + join after the grouped down */
-    MOE_FFN_K_COUNT = 8
+    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit) */
+    MOE_FFN_K_ROUTE = 1,        /* softmax, top-k, renormalisation, bucketing, job records */
+    MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
+    MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
+    MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone */
+    MOE_FFN_K_SH_DOWN = 5,      /* down of the shared expert alone */
+    MOE_FFN_K_JOIN = 6,         /* weighted sum over slots + sigmoid-gated shared output */
+    MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up */
+    MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down */
+    MOE_FFN_K_COUNT = 9
 } moe_ffn_kernel_id;
 
 int32_t moe_ffn_abi_version(void);
@@ -216,8 +217,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t plan, const moe_ffn_tensors *tenso
                                int32_t n_tokens, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
-/* Releases the plan, its stream, events and counters (waits for the plan's
- * own stream to drain).  NULL is a no-op. */
+/* Releases the plan, its stream and events (waits for the plan's own stream
+ * to drain).  NULL is a no-op. */
 void moe_ffn_destroy(moe_ffn_plan_t plan);
 
 /* Profiling hooks for the benchmark.  While enabled, every later forward

@@ -1,16 +1,19 @@
 // forward.cpp -- moe_ffn_forward / moe_ffn_destroy / profiling hooks.
 //
-// Order of work on the GPU for one forward (mat-vec regime):
-//   AUX   (the shared expert overlaps the routed chain; page "ggml-cuda: overlap
-//          the MoE shared expert on a separate stream", section "What this
-//          changes": one fork at the input, one join before the add)
-//            stream: record fork
-//            aux:    wait fork -> shared gate/up -> shared down (S) -> record join
-//            stream: router+top-k+bucketing -> routed gate/up -> wait join -> down+join
-//   SEQ   the same kernels, all on `stream`, shared branch first
-//   FUSED router+top-k+bucketing -> gate/up (routed + shared tiles in one grid)
-//          -> down (routed + shared rows, then the join) -- three launches
-// All three run identical per-element arithmetic, so their outputs are
+// Kernels of one forward (mat-vec regime):
+//   router  logits of E router rows and of the shared-gate vector
+//   route   softmax, top-k, renormalisation, bucketing, job records
+//   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
+//   down    y = down h per pair [+ S for the shared expert]
+//   join    out = sum_j w_j y_j + s * S
+// Where the shared expert's gate/up and down run (page "ggml-cuda: overlap the
+// MoE shared expert on a separate stream", section "What this changes": one
+// fork at the input, one join before the add):
+//   AUX   on the plan's second stream, forked from `stream` at entry and joined
+//         by an event just before the join kernel
+//   SEQ   the same kernels on `stream`, before the routed chain
+//   FUSED as extra jobs of the routed gate/up and down launches
+// Every mode runs the same per-element arithmetic, so their outputs are
 // bit-identical (the pages' requirement that the overlapped output equal the
 // sequential one).
 #include <algorithm>
@@ -72,17 +75,17 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
     if (cs != hipStreamCaptureStatusNone)
         return set_error(MOE_FFN_ERR_UNSUPPORTED,
-                         "the first forward of a plan creates its stream/events/counters and must not be captured");
+                         "the first forward of a plan creates its stream and events and must not be captured");
     if ((e = hipStreamCreateWithFlags(&P->aux, hipStreamNonBlocking)) != hipSuccess)
         return hip_fail(e, "hipStreamCreateWithFlags");
     if ((e = hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "hipEventCreateWithFlags");
     if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "hipEventCreateWithFlags");
-    if ((e = hipMalloc(&P->counters, kCounterInts * sizeof(int))) != hipSuccess)
-        return hip_fail(e, "hipMalloc(counters)");
-    if ((e = hipMemsetAsync(P->counters, 0, kCounterInts * sizeof(int), stream)) != hipSuccess)
-        return hip_fail(e, "hipMemsetAsync(counters)");
+    if ((e = hipDeviceGetAttribute(&P->cu_count, hipDeviceAttributeMultiprocessorCount, P->d.device)) != hipSuccess)
+        return hip_fail(e, "hipDeviceGetAttribute");
+    P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
+    P->occ_d = expert_kernel_occupancy(false, P->wkind, P->map_down, 0);
     P->ready = true;
     return MOE_FFN_OK;
 }
@@ -178,88 +181,91 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     float *gate_s = (float *)(W + L.gate_s), *wts = (float *)(W + L.wts);
     int *ids = (int *)(W + L.ids), *n_unique = (int *)(W + L.n_unique);
     int *pairs = (int *)(W + L.pairs), *pos_expert = (int *)(W + L.pos_expert);
-    int4 *slots = (int4 *)(W + L.slots);
-    float *logits = (float *)(W + L.logits), *h = (float *)(W + L.h);
+    int *records = (int *)(W + L.records);
+    float *logits = (float *)(W + L.logits), *h = (float *)(W + L.h), *y = (float *)(W + L.y);
 
-    const uint32_t mode = P->mode_matvec;
+    const uint32_t mode = n_tokens <= P->matvec_max ? P->mode_matvec : P->mode_gemm;
     const int Ti = n_tokens;
 
-    // router + top-k + bucketing
     RouterParams rp{};
     rp.x = t->x;
     rp.x_bf16 = d.x_dtype == MOE_FFN_BF16;
-    rp.T = Ti; rp.H = (int)H; rp.E = (int)E; rp.k = (int)k;
-    rp.router = t->w_router; rp.gate_vec = t->gate_vec;
-    rp.logits = logits; rp.ids = ids; rp.wts = wts; rp.gate_s = gate_s;
-    rp.slots = slots; rp.n_unique = n_unique; rp.pairs = pairs; rp.pos_expert = pos_expert;
-    rp.counters = P->counters;
+    rp.T = Ti; rp.H = (int)H; rp.E = (int)E;
+    rp.router = t->w_router; rp.gate_vec = t->gate_vec; rp.logits = logits;
     rp.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
-    // small batches: the routed gate/up workgroups rank the batch themselves
-    const bool route_in_gu = Ti <= kRouteInGateUpMaxT;
-    rp.route = route_in_gu ? 0 : 1;
-    rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
-    rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
     const int r_rows = router_rows_per_wg(P->map_router);
     const int r_grid = (int)((E + 1 + r_rows - 1) / r_rows);
     const int r_tiles = (Ti + rp.tok_tile - 1) / rp.tok_tile;
 
-    // gate/up
-    const size_t gu_rb = row_bytes_of(wk, (int)H);
+    RouteParams qp{};
+    qp.logits = logits; qp.T = Ti; qp.E = (int)E; qp.k = (int)k;
+    qp.ids = ids; qp.wts = wts; qp.gate_s = gate_s; qp.records = records; qp.n_unique = n_unique;
+    qp.pairs = pairs; qp.pos_expert = pos_expert;
+    qp.dbg_ids = t->dbg_topk_ids; qp.dbg_w = t->dbg_topk_weights;
+    qp.dbg_logits = t->dbg_logits; qp.dbg_gate = t->dbg_shared_gate;
+
     GateUpParams gp{};
     gp.x = t->x; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
-    gp.tok_per_pass = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
+    gp.x_resident = (size_t)Ti * H * xb <= kStageBytes ? 1 : 0;
+    gp.tok_per_pass = std::max(1, (int)(kStageBytes / (H * xb)));
     gp.wg = (const uint8_t *)t->w_gate; gp.wu = (const uint8_t *)t->w_up;
     gp.sg = t->w_gate_scale; gp.su = t->w_up_scale; gp.I = (int)I;
-    gp.route_here = route_in_gu ? 1 : 0;
-    gp.logits = logits; gp.ids = ids; gp.wts = wts; gp.gate_s = gate_s;
-    gp.slots = slots; gp.n_unique = n_unique; gp.pairs = pairs; gp.pos_expert = pos_expert;
-    gp.dbg_ids = t->dbg_topk_ids; gp.dbg_w = t->dbg_topk_weights;
-    gp.dbg_logits = t->dbg_logits; gp.dbg_gate = t->dbg_shared_gate;
-    gp.h = h;
+    gp.records = records; gp.n_unique = n_unique; gp.pairs = pairs; gp.h = h;
     gp.swg = (const uint8_t *)t->sh_gate; gp.swu = (const uint8_t *)t->sh_up;
     gp.ssg = t->sh_gate_scale; gp.ssu = t->sh_up_scale; gp.Is = (int)Is; gp.hs = sh_h;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
-    const int tiles_r = (int)((I + gu_rows - 1) / gu_rows);
-    const int tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
-    const int max_slots = (int)std::min(E, T * k);
-    (void)gu_rb;
+    gp.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
+    const int gu_tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
+    const int max_used = (int)std::min(E, T * k);
 
-    // down
     DownParams dp{};
     dp.T = Ti; dp.H = (int)H; dp.k = (int)k; dp.E = (int)E;
     dp.wd = (const uint8_t *)t->w_down; dp.sd = t->w_down_scale; dp.I = (int)I;
-    dp.h = h; dp.pairs = pairs; dp.pos_expert = pos_expert;
-    dp.swd = (const uint8_t *)t->sh_down; dp.ssd = t->sh_down_scale; dp.Is = (int)Is; dp.hs = sh_h;
-    dp.wts = wts; dp.gate_s = gate_s; dp.S_in = sh_S; dp.S_out = sh_S; dp.out = t->out;
+    dp.h = h; dp.records = records; dp.n_unique = n_unique; dp.pairs = pairs; dp.y = y;
+    dp.swd = (const uint8_t *)t->sh_down; dp.ssd = t->sh_down_scale; dp.Is = (int)Is;
+    dp.hs = sh_h; dp.S = sh_S;
     const int d_rows = down_rows_per_wg(wk, P->map_down);
-    const int d_grid = (int)((H + d_rows - 1) / d_rows);
+    dp.tiles_routed = (int)((H + d_rows - 1) / d_rows);
+    const int d_tiles_s = dp.tiles_routed;
+
+    JoinParams jp{};
+    jp.T = Ti; jp.H = (int)H; jp.k = (int)k; jp.y = y; jp.wts = wts; jp.gate_s = gate_s;
+    jp.S = sh_S; jp.out = t->out;
 
     const bool delay_main = d.flags & MOE_FFN_DEBUG_DELAY_MAIN;
     const bool delay_aux = d.flags & MOE_FFN_DEBUG_DELAY_AUX;
     const uint64_t delay_ticks = 20000;  // 200 us of the 100 MHz constant clock
 
     auto run_router = [&](hipStream_t s) {
-        return timed(P, MOE_FFN_K_ROUTER, s,
-                     [&] { return launch_router(rp, P->map_router, r_grid, r_tiles, s); });
+        hipError_t e1 = timed(P, MOE_FFN_K_ROUTER, s,
+                              [&] { return launch_router(rp, P->map_router, r_grid, r_tiles, s); });
+        if (e1 != hipSuccess) return e1;
+        return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(qp, s); });
     };
+    // grid of a grid-stride expert launch: its jobs, capped at the resident workgroups
+    auto expert_grid = [&](int jobs, int occ) { return std::max(1, std::min(jobs, occ * P->cu_count)); };
     auto run_gate_up = [&](hipStream_t s, bool routed, bool shared) {
         GateUpParams g = gp;
-        g.routed_slots = routed ? max_slots : 0;
-        g.tiles_routed = tiles_r;
-        g.tiles_shared = shared ? tiles_s : 0;
-        const int grid = g.tiles_shared + g.routed_slots * g.tiles_routed;
+        g.routed = routed ? 1 : 0;
+        g.tiles_shared = shared ? gu_tiles_s : 0;
+        const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
         const int kid = routed ? MOE_FFN_K_GATE_UP : MOE_FFN_K_SH_GATE_UP;
-        return timed(P, kid, s, [&] { return launch_gate_up(g, wk, P->map_gu, gu_rows, grid, 0, s); });
-    };
-    auto run_down = [&](hipStream_t s, int dmode) {
-        DownParams q = dp;
-        q.mode = dmode;
-        q.n_routed = dmode == DOWN_SHARED_ONLY ? 0 : Ti * (int)k;
-        q.n_shared = dmode == DOWN_JOIN ? 0 : Ti;
-        const int kid = dmode == DOWN_SHARED_ONLY ? MOE_FFN_K_SH_DOWN : MOE_FFN_K_DOWN;
         return timed(P, kid, s, [&] {
-            return launch_down(q, wk, P->map_down, d_rows, d_grid, 0, s);
+            return launch_gate_up(g, wk, P->map_gu, expert_grid(jobs, P->occ_gu), s);
         });
+    };
+    auto run_down = [&](hipStream_t s, bool routed, bool shared) {
+        DownParams q = dp;
+        q.routed = routed ? 1 : 0;
+        q.tiles_shared = shared ? d_tiles_s : 0;
+        const int jobs = q.tiles_shared + (routed ? max_used * q.tiles_routed : 0);
+        const int kid = routed ? MOE_FFN_K_DOWN : MOE_FFN_K_SH_DOWN;
+        return timed(P, kid, s, [&] {
+            return launch_down(q, wk, P->map_down, expert_grid(jobs, P->occ_d), s);
+        });
+    };
+    auto run_join = [&](hipStream_t s) {
+        return timed(P, MOE_FFN_K_JOIN, s, [&] { return launch_join(jp, s); });
     };
 
     hipError_t err = hipSuccess;
@@ -271,26 +277,29 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         chk(hipStreamWaitEvent(P->aux, P->ev_fork, 0));
         if (delay_aux) chk(launch_delay(P->aux, delay_ticks));
         chk(run_gate_up(P->aux, false, true));
-        chk(run_down(P->aux, DOWN_SHARED_ONLY));
+        chk(run_down(P->aux, false, true));
         chk(hipEventRecord(P->ev_join, P->aux));
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(run_gate_up(stream, true, false));
+        chk(run_down(stream, true, false));
         chk(hipStreamWaitEvent(stream, P->ev_join, 0));
-        chk(run_down(stream, DOWN_JOIN));
+        chk(run_join(stream));
     } else if (mode == MOE_FFN_SHARED_SEQ) {
         if (delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(run_gate_up(stream, false, true));
-        chk(run_down(stream, DOWN_SHARED_ONLY));
+        chk(run_down(stream, false, true));
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(run_gate_up(stream, true, false));
-        chk(run_down(stream, DOWN_JOIN));
+        chk(run_down(stream, true, false));
+        chk(run_join(stream));
     } else {  // FUSED
         if (delay_main || delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(run_gate_up(stream, true, true));
-        chk(run_down(stream, DOWN_FUSED));
+        chk(run_down(stream, true, true));
+        chk(run_join(stream));
     }
     if (err != hipSuccess) return hip_fail(err, "kernel launch");
     if ((err = hipGetLastError()) != hipSuccess) return hip_fail(err, "kernel launch");
@@ -306,10 +315,6 @@ void moe_ffn_destroy(moe_ffn_plan_t P) {
         hipEventDestroy(r.stop);
     }
     for (hipEvent_t e : P->pool) hipEventDestroy(e);
-    if (P->counters) {
-        hipDeviceSynchronize();
-        hipFree(P->counters);
-    }
     if (P->ev_fork) hipEventDestroy(P->ev_fork);
     if (P->ev_join) hipEventDestroy(P->ev_join);
     if (P->aux) hipStreamDestroy(P->aux);

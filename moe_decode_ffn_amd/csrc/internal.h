@@ -21,7 +21,6 @@ constexpr int kDefaultMatvecMax = 16;
 constexpr size_t kWsAlign = 256;
 constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
 constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
-constexpr int kCounterInts = 1024;        // 4 KiB of router tickets
 
 // weight storage as the kernels see it
 enum WKind : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
@@ -44,16 +43,15 @@ struct Layout {
     size_t gate_s = 0;     // f32 [Tmax]
     size_t ids = 0;        // i32 [Tmax*k]
     size_t wts = 0;        // f32 [Tmax*k]
-    size_t slots = 0;      // int4 [E]: (expert, first position, count, 0) per used expert
+    size_t records = 0;    // i32 [E][kRecInts]: job record per used expert
     size_t n_unique = 0;   // i32 [4]
     size_t pairs = 0;      // i32 [Tmax*k]: pair id t*k+j in expert-bucketed order
     size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
     size_t logits = 0;     // f32 [Tmax][E+1] (column E = shared-gate logit), router -> gate/up
     size_t routing_bytes = 0;
     // phase region: reused by the sequential steps
-    size_t h = 0;       // mat-vec gate/up -> down: f32 [Tmax*k][I]
-    size_t hb = 0;      // grouped GEMM gate/up -> down: bf16 [Tmax*k][I]
-    size_t y = 0;       // grouped GEMM down -> join: f32 [Tmax*k][H]
+    size_t h = 0;       // gate/up -> down: f32 [Tmax*k][I]
+    size_t y = 0;       // down -> join: f32 [Tmax*k][H] (live together with h during down)
     size_t phase_bytes = 0;
     size_t total = 0;
 };
@@ -78,7 +76,8 @@ struct moe_ffn_plan_s {
     bool ready = false;
     hipStream_t aux = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    int *counters = nullptr;
+    int cu_count = 0;       // compute units of the device
+    int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
     // profiling
     bool profiling = false;
     std::vector<moeffn::ProfRec> prof;
@@ -89,23 +88,31 @@ namespace moeffn {
 
 // ---- kernel launch parameter blocks ---------------------------------------
 
+// A job record per used expert: expert, first bucketed position, token count,
+// 0, then the first kRecPairs pair ids (t*k + j) of its bucket (-1 past count).
+constexpr int kRecInts = 16;
+constexpr int kRecPairs = kRecInts - 4;
+
 struct RouterParams {
     const void *x;
     int x_bf16;
-    int T, H, E, k;
+    int T, H, E;
     const float *router;    // [E][H]
     const float *gate_vec;  // [H] (acts as row E)
     float *logits;          // [T][E+1]
+    int tok_tile;           // tokens per workgroup column
+};
+
+struct RouteParams {
+    const float *logits;    // [T][E+1]
+    int T, E, k;
     int *ids;               // [T*k]
     float *wts;             // [T*k]
     float *gate_s;          // [T]
-    int4 *slots;            // [E]
+    int *records;           // [E][kRecInts]
     int *n_unique;          // [1]
     int *pairs;             // [T*k]
     int *pos_expert;        // [T*k]
-    int *counters;          // [n_tok_tiles + 1], zero between calls
-    int tok_tile;           // tokens per workgroup column
-    int route;              // 1: rank and bucket in this launch (ticket path)
     int32_t *dbg_ids;
     float *dbg_w, *dbg_logits, *dbg_gate;
 };
@@ -113,84 +120,74 @@ struct RouterParams {
 struct GateUpParams {
     const void *x;
     int T, H, k, E;
-    int tok_per_pass;  // tokens staged in LDS per pass
+    int x_resident;                // 1: all T tokens staged in LDS once
+    int tok_per_pass;              // else: tokens staged per pass
     // routed experts
     const uint8_t *wg, *wu;        // [E][I] rows
     const uint16_t *sg, *su;       // Q4 scales [E][I][H/32]
     int I;
-    // routing: read (route_here = 0) or computed by every routed workgroup from
-    // the logits and published by the first one (route_here = 1)
-    int route_here;
-    const float *logits;           // [T][E+1]
-    int *ids;                      // [T*k]
-    float *wts;                    // [T*k]
-    float *gate_s;                 // [T]
-    int4 *slots;
-    int *n_unique;
-    int *pairs;
-    int *pos_expert;
-    int32_t *dbg_ids;
-    float *dbg_w, *dbg_logits, *dbg_gate;
+    const int *records;
+    const int *n_unique;
+    const int *pairs;
     float *h;                      // [T*k][I]
-    int routed_slots;              // expert slots in the grid
-    int tiles_routed;              // workgroup tiles per routed expert
+    int routed;                    // routed experts' jobs are in this launch
+    int tiles_routed;              // jobs per routed expert
     // shared expert
     const uint8_t *swg, *swu;
     const uint16_t *ssg, *ssu;
     int Is;
     float *hs;                     // [T][Is]
-    int tiles_shared;              // 0 = shared expert not in this launch
+    int tiles_shared;              // jobs of the shared expert (0 = not in this launch)
 };
-
-enum DownMode : int { DOWN_FUSED = 0, DOWN_JOIN = 1, DOWN_SHARED_ONLY = 2 };
 
 struct DownParams {
     int T, H, k, E;
-    int pos_per_pass;  // activation vectors staged in LDS per pass (set by the launcher)
-    int mode;
     // routed experts
     const uint8_t *wd;   // [E][H] rows of I
     const uint16_t *sd;  // [E][H][I/32]
     int I;
     const float *h;      // [T*k][I]
+    const int *records;
+    const int *n_unique;
     const int *pairs;
-    const int *pos_expert;
-    int n_routed;        // routed positions in this launch (T*k or 0)
+    float *y;            // [T*k][H]
+    int routed;
+    int tiles_routed;
     // shared expert
     const uint8_t *swd;  // [H] rows of Is
     const uint16_t *ssd; // [H][Is/32]
     int Is;
     const float *hs;     // [T][Is]
-    int n_shared;        // shared positions in this launch (T or 0)
-    // join
+    float *S;            // [T][H]
+    int tiles_shared;
+};
+
+struct JoinParams {
+    int T, H, k;
+    const float *y;      // [T*k][H]
     const float *wts;    // [T*k]
     const float *gate_s; // [T]
-    const float *S_in;   // [T][H] (DOWN_JOIN)
-    float *S_out;        // [T][H] (DOWN_SHARED_ONLY)
+    const float *S;      // [T][H]
     float *out;          // [T][H]
 };
 
 // ---- launchers (kernel files) -------------------------------------------
 hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
                          hipStream_t s);
-hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int rows_per_wg,
-                          int grid, size_t lds, hipStream_t s);
-hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int rows_per_wg, int grid,
-                       size_t lds, hipStream_t s);
+hipError_t launch_route(const RouteParams &p, hipStream_t s);
+hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
+hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
+hipError_t launch_join(const JoinParams &p, hipStream_t s);
 hipError_t launch_delay(hipStream_t s, uint64_t ticks);
 
 // rows each workgroup covers for a kernel family and row map
 int router_rows_per_wg(const RowMap &m);
 int gate_up_rows_per_wg(int wkind, const RowMap &m);
 int down_rows_per_wg(int wkind, const RowMap &m);
-// LDS of the down kernel for n_pos positions; sets the positions staged per pass
-size_t down_lds_bytes(int wkind, const RowMap &m, int I, int Is, int T, int k, int n_routed,
-                      int n_shared, int *pos_per_pass);
-// LDS of the gate/up kernel (staging + in-kernel routing when route_here)
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);
 size_t router_lds_bytes(const RouterParams &p);
-// largest batch whose routing the gate/up workgroups compute themselves
-constexpr int kRouteInGateUpMaxT = 16;
+size_t route_lds_bytes(int T, int k, int E);
+int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds);
 
 // ---- planner helpers (plan.cpp) ---------------------------------------------
 RowMap make_row_map(size_t row_bytes);

@@ -115,10 +115,13 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     if (!P) return set_error(MOE_FFN_ERR_INVALID_ARG, "out of host memory");
     P->d = d;
     P->wkind = d.weight_dtype;
-    P->matvec_max = d.max_tokens;  // only the mat-vec regime exists in this build
+    // small-batch threshold: at or below it the shared expert is folded into the
+    // routed launches (fewest launches); above it, where the shared expert's own
+    // work is large, it overlaps the routed chain on the plan's second stream
+    P->matvec_max = d.matvec_max_tokens ? d.matvec_max_tokens : kDefaultMatvecMax;
     const uint32_t mode = d.flags & MOE_FFN_SHARED_MASK;
-    P->mode_matvec = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_AUX : mode;
-    P->mode_gemm = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_SEQ : mode;
+    P->mode_matvec = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_FUSED : mode;
+    P->mode_gemm = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_AUX : mode;
 
     const int H = d.hidden, E = d.n_experts, k = d.top_k, I = d.inter, Is = d.shared_inter;
     const size_t T = (size_t)d.max_tokens, P_ = T * k;
@@ -127,18 +130,12 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     P->map_down = make_row_map(row_bytes_of(P->wkind, std::max(I, Is)));
 
     // LDS of each kernel at the largest batch it can see
-    const int Tmv = P->matvec_max;
-    const size_t lds_down = down_lds_bytes(P->wkind, P->map_down, I, Is, Tmv, k, Tmv * k, Tmv, nullptr);
-    GateUpParams gq{};
-    gq.T = std::min(Tmv, kRouteInGateUpMaxT); gq.H = H; gq.k = k; gq.E = E; gq.route_here = 1;
     const int xbytes = d.x_dtype == MOE_FFN_F32 ? 4 : 2;
-    gq.tok_per_pass = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
     RouterParams rq{};
-    rq.T = d.max_tokens; rq.H = H; rq.E = E; rq.k = k; rq.x_bf16 = xbytes == 2;
-    rq.tok_tile = gq.tok_per_pass; rq.route = 1;
+    rq.H = H; rq.x_bf16 = xbytes == 2;
+    rq.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
     const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
-    if (!maps_ok || lds_down > kLdsLimit || gate_up_lds_bytes(gq, xbytes) > kLdsLimit ||
-        router_lds_bytes(rq) > kLdsLimit) {
+    if (!maps_ok || router_lds_bytes(rq) > kLdsLimit || route_lds_bytes(d.max_tokens, k, E) > kLdsLimit) {
         delete P;
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
     }
@@ -151,20 +148,18 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.gate_s = c;     c += align_up(T * 4);
     L.ids = c;        c += align_up(P_ * 4);
     L.wts = c;        c += align_up(P_ * 4);
-    L.slots = c;      c += align_up((size_t)E * 16);
+    L.records = c;    c += align_up((size_t)E * kRecInts * 4);
     L.n_unique = c;   c += align_up(16);
     L.pairs = c;      c += align_up(P_ * 4);
     L.pos_expert = c; c += align_up(P_ * 4);
-    // logits stay live through the gate/up step, whose workgroups rank the batch
-    // while others already write h, so they cannot share the phase region
     L.logits = c;     c += align_up(T * (E + 1) * 4);
     L.routing_bytes = c - L.shared_bytes;
+    // sequential steps: gate/up holds h, down holds h and y, join holds y
     const size_t base = c;
-    const size_t ph_matvec = align_up(P_ * I * 4);
+    const size_t hb = align_up(P_ * I * 4), yb = align_up(P_ * H * 4);
     L.h = base;
-    L.hb = base;
-    L.y = base;
-    L.phase_bytes = ph_matvec;
+    L.y = base + hb;
+    L.phase_bytes = std::max({hb, hb + yb, yb});
     L.total = base + L.phase_bytes;
 
     *out_plan = P;

@@ -1,15 +1,14 @@
-// router.hip -- router GEMV (fp32 rows, row E = the shared-expert gate vector)
-// and, for batches above the small-batch limit, ranking and bucketing in the
-// same launch.
+// router.hip -- router GEMV (fp32 rows; row E is the shared-expert gate
+// vector, so its logit is sigma's argument) and the routing kernel.
 //
-// Small batches: the launch only writes the logits [T][E+1]; the routed
-// gate/up workgroups rank the batch themselves (routing.h), one dependent
-// memory round trip instead of three.
-// Larger batches (ticket path): the last workgroup of each token tile
-// (integer ticket, no spinning) ranks that tile's tokens, one wave per token;
-// the last tile then buckets every (token, slot) pair.  Each workgroup makes
-// its logits visible with one device-scope fence after all its stores have
-// completed, and tickets reset themselves, so the launch can be replayed.
+// k_router: logits [T][E+1]; workgroups tile (rows x tokens), no cross-
+//   workgroup communication.
+// k_route: one workgroup of 1024 threads ranks every token (one wave per
+//   token, routing.h), buckets the (token, slot) pairs by expert and writes
+//   the tables the expert kernels read: ids and weights per slot, the gate
+//   value per token, and one 64-byte job record per used expert
+//   (expert, first position, count, 0, first 12 pair ids) so an expert
+//   workgroup learns everything about its job from one scalar load.
 #include "device.h"
 #include "internal.h"
 #include "routing.h"
@@ -17,6 +16,7 @@
 namespace moeffn {
 
 constexpr int kRouterWaves = 4;
+constexpr int kRouteThreads = 1024;
 
 int router_rows_per_wg(const RowMap &m) { return kRouterWaves * (64 / m.lpr); }
 
@@ -24,10 +24,9 @@ template <int LPR, int NC, bool XBF>
 __global__ __launch_bounds__(256) void k_router(RouterParams p) {
     constexpr int RPI = 64 / LPR;
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPR, sl = lane % LPR;
-    const int H = p.H, E = p.E, k = p.k;
+    const int H = p.H, E = p.E;
     const int n_chunks = H / 4;  // fp32 rows, 4 elements per 16-byte chunk
     const int row = (blockIdx.x * kRouterWaves + wave) * RPI + seg;
     const bool valid = row <= E;
@@ -71,52 +70,57 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         acc = seg_sum<LPR>(acc);
         if (valid && sl == 0) p.logits[(size_t)(t0 + i) * (E + 1) + row] = acc;
     }
-    if (!p.route) return;
+}
 
-    // ---- ticket path ------------------------------------------------------------------
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this workgroup has completed
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();  // one device-scope release for the workgroup
-        s_last = atomicAdd(&p.counters[blockIdx.y], 1) == (int)gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    int *r_ids = reinterpret_cast<int *>(lds);  // staging area is free now
-    for (int i = wave; i < nt; i += kRouterWaves) {
-        const int t = t0 + i;
-        RouteOut o{p.ids + t * k, p.wts + t * k, p.gate_s + t,
+__global__ __launch_bounds__(kRouteThreads) void k_route(RouteParams p) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int T = p.T, E = p.E, k = p.k, NP = T * k;
+    int *r_ids = reinterpret_cast<int *>(lds);       // [NP]
+    int *r_pairs = r_ids + NP;                       // [NP]
+    int *r_pose = r_pairs + NP;                      // [NP]
+    int *r_nu = r_pose + NP;                         // [4]
+    int4 *r_slots = reinterpret_cast<int4 *>(lds + (((size_t)(3 * NP + 4) * 4 + 15) & ~(size_t)15));
+    uint32_t *scratch = reinterpret_cast<uint32_t *>(r_slots + (E < NP ? E : NP));
+
+    for (int t = wave; t < T; t += nw) {
+        RouteOut o{r_ids + t * k, p.wts + t * k, p.gate_s + t,
                    p.dbg_ids ? p.dbg_ids + t * k : nullptr, p.dbg_w ? p.dbg_w + t * k : nullptr,
                    p.dbg_gate ? p.dbg_gate + t : nullptr,
                    p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
         route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
     }
-    if (tid == 0) atomicExch(&p.counters[blockIdx.y], 0);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (gridDim.y > 1) {
-        if (tid == 0) {
-            __threadfence();
-            s_last = atomicAdd(&p.counters[gridDim.y], 1) == (int)gridDim.y - 1;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        if (tid == 0) atomicExch(&p.counters[gridDim.y], 0);
+    bucket_pairs(r_ids, T, k, E, scratch, r_slots, r_pairs, r_pose, r_nu);
+    __syncthreads();
+    const int nu = *r_nu;
+    for (int i = tid; i < NP; i += blockDim.x) {
+        p.ids[i] = r_ids[i];
+        p.pairs[i] = r_pairs[i];
+        p.pos_expert[i] = r_pose[i];
     }
-    // all ids of the batch into LDS, then bucket them there
-    const int NP = p.T * k;
-    for (int q = tid; q < NP; q += 256) r_ids[q] = p.ids[q];
-    __syncthreads();
-    bucket_pairs(r_ids, p.T, k, E, reinterpret_cast<uint32_t *>(r_ids + NP), p.slots, p.pairs,
-                 p.pos_expert, p.n_unique);
+    for (int i = tid; i < nu * kRecInts; i += blockDim.x) {
+        const int u = i / kRecInts, f = i - u * kRecInts;
+        const int4 s = r_slots[u];
+        int v;
+        if (f == 0) v = s.x;
+        else if (f == 1) v = s.y;
+        else if (f == 2) v = s.z;
+        else if (f == 3) v = 0;
+        else v = (f - 4 < s.z) ? r_pairs[s.y + f - 4] : -1;
+        p.records[i] = v;
+    }
+    if (tid == 0) *p.n_unique = nu;
 }
 
 size_t router_lds_bytes(const RouterParams &p) {
-    const size_t stage = (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
-    const size_t route = p.route ? (size_t)(p.T * p.k + bucket_scratch_ints(p.E, p.T)) * 4 : 0;
-    return stage > route ? stage : route;
+    return (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
+}
+
+size_t route_lds_bytes(int T, int k, int E) {
+    const int np = T * k;
+    return (((size_t)(3 * np + 4) * 4 + 15) & ~(size_t)15) + (size_t)(E < np ? E : np) * 16 +
+           (size_t)bucket_scratch_ints(E, T) * 4;
 }
 
 template <int LPR, int NC>
@@ -133,7 +137,6 @@ static hipError_t launch_router_t(const RouterParams &p, int grid_rows, int grid
 
 hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
                          hipStream_t s) {
-    if (grid_tiles + 1 > kCounterInts) return hipErrorInvalidValue;
     if (router_lds_bytes(p) > kLdsLimit) return hipErrorInvalidValue;
     switch (m.lpr * 100 + m.nc) {
     case 801: return launch_router_t<8, 1>(p, grid_rows, grid_tiles, s);
@@ -147,6 +150,15 @@ hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, 
     case 6432: return launch_router_t<64, 32>(p, grid_rows, grid_tiles, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_route(const RouteParams &p, hipStream_t s) {
+    const size_t lds = route_lds_bytes(p.T, p.k, p.E);
+    if (lds > kLdsLimit) return hipErrorInvalidValue;
+    // one wave per token up to 16 waves
+    const int waves = p.T < 16 ? (p.T < 4 ? 4 : p.T) : 16;
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * waves), lds, s, p);
+    return hipGetLastError();
 }
 
 // ---- bounded delay (test hook) ------------------------------------------------------

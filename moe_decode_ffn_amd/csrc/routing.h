@@ -104,40 +104,40 @@ __device__ __forceinline__ void route_token_any(const float *lg, int E, int k, i
 
 // LDS ints the bucketing needs for E experts and T tokens.
 __host__ __device__ inline int bucket_scratch_ints(int E, int T) {
-    return E * ((T + 31) / 32) + 3 * E + 16;
+    return E * ((T + 31) / 32) + 2 * E + 2 * 16 + 16;
 }
 
-// Bucketing of all T*k pairs by one workgroup of 256 threads.  ids[] may be
-// in LDS or global memory.  Outputs (any memory): slots[u] = (expert,
-// first position, count, 0) for used experts in ascending order, pairs[pos]
-// = t*k + j, pos_expert[pos], *n_unique.  Positions are expert-major,
-// tokens ascending within an expert; a token's rank in its expert's bucket is
-// the number of earlier tokens in the expert's token bitmap (a token picks an
-// expert at most once).  Integer only, so the result is unique.
+// Bucketing of all T*k pairs by one workgroup (any multiple of 64 threads up
+// to 1024).  ids[] may be in LDS or global memory.  Outputs (any memory):
+// slots[u] = (expert, first position, count, 0) for used experts in ascending
+// order, pairs[pos] = t*k + j, pos_expert[pos], *n_unique.  Positions are
+// expert-major, tokens ascending within an expert; a token's rank in its
+// expert's bucket is the number of earlier tokens in the expert's token bitmap
+// (a token picks an expert at most once).  Integer only: the result is unique.
 __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scratch, int4 *slots,
                              int *pairs, int *pos_expert, int *n_unique) {
-    constexpr int kWavesB = 4;
+    const int nth = blockDim.x, nw = nth >> 6;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int NP = T * k, W = (T + 31) / 32;
     uint32_t *mask = scratch;                     // [E][W] token bitmaps
     int *cnt = (int *)(mask + (size_t)E * W);     // [E]
     int *off = cnt + E;                           // [E] first position of expert e
-    int *wtot = off + E + E;                      // [2 * waves]
-    for (int i = tid; i < E * W; i += 256) mask[i] = 0u;
+    int *wtot = off + E;                          // [2 * 16] wave totals
+    for (int i = tid; i < E * W; i += nth) mask[i] = 0u;
     __syncthreads();
-    for (int q = tid; q < NP; q += 256) {
+    for (int q = tid; q < NP; q += nth) {
         const int t = q / k, e = ids[q];
         if (e >= 0 && e < E) atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += nth) {
         int c = 0;
         for (int w = 0; w < W; ++w) c += __popc(mask[e * W + w]);
         cnt[e] = c;
     }
     __syncthreads();
     // exclusive scans of cnt[] and (cnt[] > 0); thread owns EPT consecutive experts
-    const int EPT = (E + 255) / 256;
+    const int EPT = (E + nth - 1) / nth;
     int a = 0, b = 0;
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
@@ -148,10 +148,10 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
         const int ya = __shfl_up(ia, d), yb = __shfl_up(ib, d);
         if (lane >= d) { ia += ya; ib += yb; }
     }
-    if (lane == 63) { wtot[wave] = ia; wtot[kWavesB + wave] = ib; }
+    if (lane == 63) { wtot[wave] = ia; wtot[16 + wave] = ib; }
     __syncthreads();
     int ba = ia - a, bb = ib - b;
-    for (int w = 0; w < wave; ++w) { ba += wtot[w]; bb += wtot[kWavesB + w]; }
+    for (int w = 0; w < wave; ++w) { ba += wtot[w]; bb += wtot[16 + w]; }
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
         if (e < E) {
@@ -161,13 +161,13 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
             bb += cnt[e] > 0;
         }
     }
-    if (tid == 255) {
+    if (tid == nth - 1) {
         int nu = 0;
-        for (int w = 0; w < kWavesB; ++w) nu += wtot[kWavesB + w];
+        for (int w = 0; w < nw; ++w) nu += wtot[16 + w];
         *n_unique = nu;
     }
     __syncthreads();
-    for (int q = tid; q < NP; q += 256) {
+    for (int q = tid; q < NP; q += nth) {
         const int t = q / k, e = ids[q];
         if (e < 0 || e >= E) continue;
         const uint32_t *me = mask + e * W;

@@ -26,7 +26,8 @@ SHARED_AUTO, SHARED_AUX, SHARED_SEQ, SHARED_FUSED, SHARED_MASK = 0x0, 0x1, 0x2, 
 FORCE_MATVEC, FORCE_GEMM = 0x10, 0x20
 DEBUG_DELAY_AUX, DEBUG_DELAY_MAIN = 0x100, 0x200
 # moe_ffn_kernel_id
-KERNELS = ("router", "gate_up", "down", "sh_gate_up", "sh_down", "gg_gate_up", "gg_down", "gg_join")
+KERNELS = ("router", "route", "gate_up", "down", "sh_gate_up", "sh_down", "join", "gg_gate_up",
+           "gg_down")
 K_COUNT = len(KERNELS)
 
 DTYPES = {"f32": F32, "bf16": BF16, "q4": Q4_B32}

@@ -119,13 +119,16 @@ def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
     shared = _align(T * Is * 4) + _align(T * H * 4)
-    # logits are read by the gate/up workgroups while others write h: routing region
-    routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 16) + _align(16)
+    # routing region: gate, ids, weights, one 64-byte job record per expert, used-expert
+    # count, bucketed pairs and their experts, logits [T][E+1]
+    routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
                + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4))
-    phases = {"mat-vec h": _align(T * k * I * 4)}
+    h, y = _align(T * k * I * 4), _align(T * k * H * 4)
+    phases = {"gate/up": h, "down": h + y, "join": y}  # live scratch of each sequential step
     assert info.shared_region_bytes == shared
     assert info.routing_region_bytes == routing
     assert info.phase_region_bytes == max(phases.values())
+    assert info.phase_region_bytes < sum(phases.values())
     assert ws == info.workspace_bytes == shared + routing + max(phases.values())
 
 
@@ -133,7 +136,11 @@ def test_auto_mode_defaults(lib):
     plan, _ = ffn.moe_ffn_plan(desc())
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
-    assert info.shared_mode_matvec in (ffn.SHARED_AUX, ffn.SHARED_SEQ, ffn.SHARED_FUSED)
+    # measured on MI355X: folding the shared expert into the routed launches wins at
+    # small batches, overlapping it on the second stream wins above the threshold
+    assert info.matvec_max_tokens == 16
+    assert info.shared_mode_matvec == ffn.SHARED_FUSED
+    assert info.shared_mode_gemm == ffn.SHARED_AUX
     for m in (ffn.SHARED_AUX, ffn.SHARED_SEQ, ffn.SHARED_FUSED):
         plan, _ = ffn.moe_ffn_plan(desc(flags=m))
         assert ffn.moe_ffn_plan_get_info(plan).shared_mode_matvec == m
