@@ -60,6 +60,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="decode_bf16_t1")
     ap.add_argument("--mode", default="auto", choices=["auto", "aux", "seq", "fused"])
+    ap.add_argument("--regime", default="auto", choices=["auto", "matvec", "gemm"])
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -89,7 +90,8 @@ def main() -> int:
     L = LAYER_COPIES[shape.w_dtype] if shape.hidden >= 1024 else 2
     layers = [synth.make_layer_device(shape, 100 + i, dev) for i in range(L)]
     xs = [synth.make_tokens_device(shape, T, 1000 + j, dev) for j in range(TOKEN_POOL)]
-    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=mode)
+    regime = {"auto": 0, "matvec": ffn.FORCE_MATVEC, "gemm": ffn.FORCE_GEMM}[args.regime]
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=mode | regime)
     info = mf.info()
     ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
@@ -165,8 +167,11 @@ def main() -> int:
     torch.cuda.synchronize()
     prof = mf.profile_read()
     mf.profile_enable(False)
-    shared_mode = {1: "aux", 2: "seq", 3: "fused"}[info.shared_mode_matvec]
-    dominant = "gate_up"  # the routed (+ shared when fused) gate/up launch moves the most bytes
+    small = T <= info.matvec_max_tokens
+    shared_mode = {1: "aux", 2: "seq", 3: "fused"}[info.shared_mode_matvec if small else info.shared_mode_gemm]
+    # the routed (+ shared when fused) gate/up launch moves the most bytes; its name
+    # says which regime ran (mat-vec or grouped GEMM)
+    dominant = "gg_gate_up" if prof["gg_gate_up"][1] else "gate_up"
     ms_tot, n_launch = prof[dominant]
     avg_us = ms_tot * 1e3 / max(1, n_launch)
     gu_units = unique_mean + (1 if shared_mode == "fused" else 0)
@@ -220,6 +225,7 @@ def main() -> int:
                    "top_k": shape.top_k, "inter": shape.inter, "shared_inter": shape.shared_inter,
                    "tokens": T, "weights": shape.w_dtype, "accumulate": "fp32",
                    "layer_copies": L, "shared_mode": shared_mode,
+                   "regime": "gemm" if dominant == "gg_gate_up" else "matvec",
                    "launch": "eager" if args.eager else "hip_graph"},
         "expert_weight_GBps": round(gbps, 1),
         "expert_weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),

@@ -89,7 +89,13 @@ typedef enum moe_ffn_dtype {
 #define MOE_FFN_SHARED_FUSED 0x3u  /* shared expert folded into the routed kernels' grids (fewest launches) */
 #define MOE_FFN_SHARED_MASK 0x3u
 /* Regime: mat-vec kernels while n_tokens <= desc.matvec_max_tokens, grouped
- * MFMA GEMM above it.  The FORCE flags pin one regime for every n_tokens. */
+ * MFMA GEMM above it where the storage is (BF16, BF16) with hidden, inter and
+ * shared_inter multiples of 128 (other storage stays on the mat-vec kernels).
+ * The FORCE flags pin one regime for every n_tokens; FORCE_GEMM on storage the
+ * GEMM does not take is MOE_FFN_ERR_UNSUPPORTED at planning.  The GEMM regime
+ * rounds the SwiGLU activation to bf16 before the down product; the mat-vec
+ * regime keeps it in fp32.  The shared-expert modes agree bit for bit within
+ * a regime. */
 #define MOE_FFN_FORCE_MATVEC 0x10u
 #define MOE_FFN_FORCE_GEMM 0x20u
 /* Test hooks: a bounded (about 200 us) spin kernel at the head of the aux
@@ -166,11 +172,11 @@ typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_ROUTE = 1,        /* softmax, top-k, renormalisation, bucketing, job records */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
-    MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone */
-    MOE_FFN_K_SH_DOWN = 5,      /* down of the shared expert alone */
+    MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */
+    MOE_FFN_K_SH_DOWN = 5,      /* down of the shared expert alone (either regime) */
     MOE_FFN_K_JOIN = 6,         /* weighted sum over slots + sigmoid-gated shared output */
-    MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up */
-    MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down */
+    MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up (routed, or routed + shared when fused) */
+    MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down (routed, or routed + shared when fused) */
     MOE_FFN_K_COUNT = 9
 } moe_ffn_kernel_id;
 

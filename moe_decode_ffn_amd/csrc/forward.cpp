@@ -1,11 +1,13 @@
 // forward.cpp -- moe_ffn_forward / moe_ffn_destroy / profiling hooks.
 //
-// Kernels of one forward (mat-vec regime):
+// Kernels of one forward:
 //   router  logits of E router rows and of the shared-gate vector
 //   route   softmax, top-k, renormalisation, bucketing, job records
 //   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
 //   down    y = down h per pair [+ S for the shared expert]
 //   join    out = sum_j w_j y_j + s * S
+// gate/up and down are mat-vec kernels (matvec.hip) up to matvec_max tokens and
+// grouped MFMA GEMMs (gemm.hip) above it when the storage is bf16.
 // Where the shared expert's gate/up and down run (page "ggml-cuda: overlap the
 // MoE shared expert on a separate stream", section "What this changes": one
 // fork at the input, one join before the add):
@@ -86,6 +88,11 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
     P->occ_d = expert_kernel_occupancy(false, P->wkind, P->map_down, 0);
+    if (P->gemm_ok)
+        for (int i = 0; i < 3; ++i) {
+            P->occ_gg_gu[i] = gg_occupancy(true, 1 << i);
+            P->occ_gg_d[i] = gg_occupancy(false, 1 << i);
+        }
     P->ready = true;
     return MOE_FFN_OK;
 }
@@ -185,6 +192,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     float *logits = (float *)(W + L.logits), *h = (float *)(W + L.h), *y = (float *)(W + L.y);
 
     const uint32_t mode = n_tokens <= P->matvec_max ? P->mode_matvec : P->mode_gemm;
+    const bool gemm = P->gemm_ok && ((d.flags & MOE_FFN_FORCE_GEMM) || n_tokens > P->matvec_max);
     const int Ti = n_tokens;
 
     RouterParams rp{};
@@ -228,6 +236,16 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     dp.tiles_routed = (int)((H + d_rows - 1) / d_rows);
     const int d_tiles_s = dp.tiles_routed;
 
+    // grouped-GEMM regime: h is kept in bf16 (the down GEMM's operand) in the same regions
+    GGParams gg{};
+    gg.x = t->x; gg.T = Ti; gg.H = (int)H; gg.k = (int)k; gg.E = (int)E; gg.I = (int)I;
+    gg.Is = (int)Is; gg.records = records; gg.n_unique = n_unique; gg.pairs = pairs;
+    gg.hb = (uint16_t *)h; gg.shb = (uint16_t *)sh_h; gg.y = y; gg.S = sh_S;
+    const int gg_rows = gg_rows_per_job();
+    // tokens per pass of a shared-expert job: 16, 32 or 64 (routed buckets are small: 16)
+    const int nt_shared = Ti <= 16 ? 1 : Ti <= 32 ? 2 : 4;
+    auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
+
     JoinParams jp{};
     jp.T = Ti; jp.H = (int)H; jp.k = (int)k; jp.y = y; jp.wts = wts; jp.gate_s = gate_s;
     jp.S = sh_S; jp.out = t->out;
@@ -264,6 +282,40 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
             return launch_down(q, wk, P->map_down, expert_grid(jobs, P->occ_d), s);
         });
     };
+    auto run_gg_gate_up = [&](hipStream_t s, bool routed, bool shared) {
+        GGParams g = gg;
+        g.w0 = (const uint8_t *)t->w_gate; g.w1 = (const uint8_t *)t->w_up;
+        g.sw0 = (const uint8_t *)t->sh_gate; g.sw1 = (const uint8_t *)t->sh_up;
+        g.routed = routed ? 1 : 0;
+        g.tiles_routed = (int)((I + gg_rows - 1) / gg_rows);
+        g.tiles_shared = shared ? (int)((Is + gg_rows - 1) / gg_rows) : 0;
+        const int nt = routed ? 1 : nt_shared;
+        const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
+        const int kid = routed ? MOE_FFN_K_GG_GATE_UP : MOE_FFN_K_SH_GATE_UP;
+        return timed(P, kid, s, [&] {
+            return launch_gg_gate_up(g, nt, expert_grid(jobs, P->occ_gg_gu[nt_index(nt)]), s);
+        });
+    };
+    auto run_gg_down = [&](hipStream_t s, bool routed, bool shared) {
+        GGParams g = gg;
+        g.w0 = (const uint8_t *)t->w_down; g.sw0 = (const uint8_t *)t->sh_down;
+        g.routed = routed ? 1 : 0;
+        g.tiles_routed = (int)((H + gg_rows - 1) / gg_rows);
+        g.tiles_shared = shared ? g.tiles_routed : 0;
+        const int nt = routed ? 1 : nt_shared;
+        const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
+        const int kid = routed ? MOE_FFN_K_GG_DOWN : MOE_FFN_K_SH_DOWN;
+        return timed(P, kid, s, [&] {
+            return launch_gg_down(g, nt, expert_grid(jobs, P->occ_gg_d[nt_index(nt)]), s);
+        });
+    };
+    // one step of the layer in the regime of this call
+    auto step_gate_up = [&](hipStream_t s, bool routed, bool shared) {
+        return gemm ? run_gg_gate_up(s, routed, shared) : run_gate_up(s, routed, shared);
+    };
+    auto step_down = [&](hipStream_t s, bool routed, bool shared) {
+        return gemm ? run_gg_down(s, routed, shared) : run_down(s, routed, shared);
+    };
     auto run_join = [&](hipStream_t s) {
         return timed(P, MOE_FFN_K_JOIN, s, [&] { return launch_join(jp, s); });
     };
@@ -276,29 +328,29 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         chk(hipEventRecord(P->ev_fork, stream));
         chk(hipStreamWaitEvent(P->aux, P->ev_fork, 0));
         if (delay_aux) chk(launch_delay(P->aux, delay_ticks));
-        chk(run_gate_up(P->aux, false, true));
-        chk(run_down(P->aux, false, true));
+        chk(step_gate_up(P->aux, false, true));
+        chk(step_down(P->aux, false, true));
         chk(hipEventRecord(P->ev_join, P->aux));
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
-        chk(run_gate_up(stream, true, false));
-        chk(run_down(stream, true, false));
+        chk(step_gate_up(stream, true, false));
+        chk(step_down(stream, true, false));
         chk(hipStreamWaitEvent(stream, P->ev_join, 0));
         chk(run_join(stream));
     } else if (mode == MOE_FFN_SHARED_SEQ) {
         if (delay_aux) chk(launch_delay(stream, delay_ticks));
-        chk(run_gate_up(stream, false, true));
-        chk(run_down(stream, false, true));
+        chk(step_gate_up(stream, false, true));
+        chk(step_down(stream, false, true));
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
-        chk(run_gate_up(stream, true, false));
-        chk(run_down(stream, true, false));
+        chk(step_gate_up(stream, true, false));
+        chk(step_down(stream, true, false));
         chk(run_join(stream));
     } else {  // FUSED
         if (delay_main || delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
-        chk(run_gate_up(stream, true, true));
-        chk(run_down(stream, true, true));
+        chk(step_gate_up(stream, true, true));
+        chk(step_down(stream, true, true));
         chk(run_join(stream));
     }
     if (err != hipSuccess) return hip_fail(err, "kernel launch");

@@ -78,6 +78,8 @@ struct moe_ffn_plan_s {
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
+    int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
+    bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
     // profiling
     bool profiling = false;
     std::vector<moeffn::ProfRec> prof;
@@ -162,6 +164,21 @@ struct DownParams {
     int tiles_shared;
 };
 
+struct GGParams {
+    const void *x;       // [T][H] bf16
+    int T, H, k, E, I, Is;
+    const uint8_t *w0, *w1;    // routed: gate and up [E][I][H] (gate/up launch) or down [E][H][I]
+    const uint8_t *sw0, *sw1;  // shared: gate and up [Is][H] or down [H][Is]
+    const int *records;
+    const int *n_unique;
+    const int *pairs;
+    uint16_t *hb;        // [T*k][I] bf16
+    uint16_t *shb;       // [T][Is] bf16
+    float *y;            // [T*k][H]
+    float *S;            // [T][H]
+    int routed, tiles_routed, tiles_shared;
+};
+
 struct JoinParams {
     int T, H, k;
     const float *y;      // [T*k][H]
@@ -178,6 +195,10 @@ hipError_t launch_route(const RouteParams &p, hipStream_t s);
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_join(const JoinParams &p, hipStream_t s);
+hipError_t launch_gg_gate_up(const GGParams &p, int nt, int grid, hipStream_t s);
+hipError_t launch_gg_down(const GGParams &p, int nt, int grid, hipStream_t s);
+int gg_occupancy(bool gate_up, int nt);
+int gg_rows_per_job();
 hipError_t launch_delay(hipStream_t s, uint64_t ticks);
 
 // rows each workgroup covers for a kernel family and row map

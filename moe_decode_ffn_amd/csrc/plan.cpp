@@ -108,13 +108,18 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
                          (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_BF16) ||
                          (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_Q4_B32);
     if (!pair_ok) return set_error(MOE_FFN_ERR_UNSUPPORTED, "unsupported (x_dtype, weight_dtype) pair");
-    if (d.flags & MOE_FFN_FORCE_GEMM)
-        return set_error(MOE_FFN_ERR_UNSUPPORTED, "grouped-GEMM regime is not available in this build");
+    // the grouped MFMA GEMM takes bf16 weights and tokens, K in chunks of 128, rows in 64s
+    const bool gemm_ok = d.weight_dtype == MOE_FFN_BF16 && d.x_dtype == MOE_FFN_BF16 &&
+                         d.hidden % 128 == 0 && d.inter % 128 == 0 && d.shared_inter % 128 == 0;
+    if ((d.flags & MOE_FFN_FORCE_GEMM) && !gemm_ok)
+        return set_error(MOE_FFN_ERR_UNSUPPORTED,
+                         "the grouped-GEMM regime needs bf16 weights and tokens and sizes that are multiples of 128");
 
     moe_ffn_plan_s *P = new (std::nothrow) moe_ffn_plan_s;
     if (!P) return set_error(MOE_FFN_ERR_INVALID_ARG, "out of host memory");
     P->d = d;
     P->wkind = d.weight_dtype;
+    P->gemm_ok = gemm_ok && !(d.flags & MOE_FFN_FORCE_MATVEC);
     // small-batch threshold: at or below it the shared expert is folded into the
     // routed launches (fewest launches); above it, where the shared expert's own
     // work is large, it overlaps the routed chain on the plan's second stream

@@ -90,6 +90,12 @@ BAD_PLANS = [
     (dict(max_tokens=257), ffn.ERR_UNSUPPORTED),
     (dict(x_dtype=ffn.F32, weight_dtype=ffn.BF16), ffn.ERR_UNSUPPORTED),
     (dict(x_dtype=ffn.BF16, weight_dtype=ffn.F32), ffn.ERR_UNSUPPORTED),
+    # the grouped GEMM takes bf16 storage with sizes that are multiples of 128
+    (dict(flags=ffn.FORCE_GEMM, weight_dtype=ffn.Q4_B32), ffn.ERR_UNSUPPORTED),
+    (dict(flags=ffn.FORCE_GEMM, x_dtype=ffn.F32, weight_dtype=ffn.F32), ffn.ERR_UNSUPPORTED),
+    (dict(flags=ffn.FORCE_GEMM, hidden=2080), ffn.ERR_UNSUPPORTED),
+    (dict(flags=ffn.FORCE_GEMM, inter=544), ffn.ERR_UNSUPPORTED),
+    (dict(flags=ffn.FORCE_GEMM, shared_inter=96), ffn.ERR_UNSUPPORTED),
 ]
 
 

@@ -33,6 +33,17 @@ SMALL = {
 }
 
 
+# grouped-GEMM regime (bf16, sizes multiples of 128), forced for every batch:
+# buckets of more than 16 tokens (several passes), shared-expert passes of
+# 16/32/64 tokens with a ragged last pass, several row tiles per expert
+SMALL_GEMM = {
+    "gemm_basic": (synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16"), 20, (1, 5, 17)),
+    "gemm_big_buckets": (synth.LayerShape(128, 2, 1, 128, 128, "bf16", "bf16"), 21, (40, 100)),
+    "gemm_many_tiles": (synth.LayerShape(512, 8, 2, 384, 640, "bf16", "bf16"), 22, (33,)),
+    "gemm_k_equals_e": (synth.LayerShape(128, 4, 4, 128, 128, "bf16", "bf16"), 23, (3, 70)),
+}
+
+
 def _plan(shape, max_tokens, mode, extra=0):
     return ffn.MoeFfn.for_shape(shape, max_tokens=max_tokens, flags=MODES[mode] | extra)
 
@@ -55,6 +66,33 @@ def test_small_layers_all_modes(orc, name):
             outs[m] = got["out"]
         assert torch.equal(outs["aux"], outs["seq"]), "aux vs sequential must be bit-identical"
         assert torch.equal(outs["aux"], outs["fused"]), "aux vs fused must be bit-identical"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_GEMM))
+def test_small_layers_gemm_regime(orc, name):
+    dev = device()
+    shape, seed, counts = SMALL_GEMM[name]
+    layer = synth.make_layer(shape, seed)
+    dl = synth.layer_to(layer, dev)
+    plans = {m: _plan(shape, max(counts), m, ffn.FORCE_GEMM) for m in MODES}
+    for T in counts:
+        x = synth.make_tokens(shape, T, seed, stream=T)
+        ref = orc.forward(oracle_layer(layer), oracle_tokens(x))
+        outs = {}
+        for m, mf in plans.items():
+            print(f"[gemm] {name} T={T} mode={m}", flush=True)
+            got = run_gpu(mf, dl, x.to(dev))
+            compare(orc, layer, x, got, tol_for(shape), ref=ref)
+            outs[m] = got["out"]
+        assert torch.equal(outs["aux"], outs["seq"]), "aux vs sequential must be bit-identical"
+        assert torch.equal(outs["aux"], outs["fused"]), "aux vs fused must be bit-identical"
+
+
+def test_force_gemm_rejected_for_other_storage():
+    for shape in (synth.TINY, synth.DECODE_Q4, synth.LayerShape(160, 12, 3, 96, 64, "bf16", "bf16")):
+        with pytest.raises(ffn.MoeFfnError) as ei:
+            ffn.MoeFfn.for_shape(shape, max_tokens=4, flags=ffn.FORCE_GEMM)
+        assert ei.value.status == ffn.ERR_UNSUPPORTED
 
 
 # ---- the decode layer at full size ----------------------------------------------------
@@ -107,23 +145,38 @@ def test_decode_layer_full_size(orc, name):
 
 
 def test_decode_bf16_t128(orc):
+    """Batch 128: the grouped-GEMM regime in every mode (bit-identical to each
+    other) and the mat-vec regime forced, each against the oracle."""
     dev = device()
     shape, seed, T = synth.DECODE_BF16, 4, 128
     dl, lc = _decode_layer(shape, seed)
     x = synth.make_tokens(shape, T, seed, stream=T)
-    print("[full] decode_bf16_t128", flush=True)
-    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
-    got = run_gpu(mf, dl, x.to(dev))
-    rep = compare(orc, lc, x, got, tol_for(shape))
+    ref = orc.forward(oracle_layer(lc), oracle_tokens(x), nthreads=oracle_threads())
+    outs = {}
+    for m in MODES:
+        print(f"[full] decode_bf16_t128 gemm mode={m}", flush=True)
+        mf = _plan(shape, T, m)
+        got = run_gpu(mf, dl, x.to(dev))
+        rep = compare(orc, lc, x, got, tol_for(shape), ref=ref)
+        print(f"  {rep}", flush=True)
+        assert rep["unique_experts"] > 200
+        outs[m] = got["out"]
+        mf.close()
+    assert torch.equal(outs["aux"], outs["seq"])
+    assert torch.equal(outs["aux"], outs["fused"])
+    print("[full] decode_bf16_t128 matvec forced", flush=True)
+    mf = _plan(shape, T, "aux", ffn.FORCE_MATVEC)
+    rep = compare(orc, lc, x, run_gpu(mf, dl, x.to(dev)), tol_for(shape), ref=ref)
     print(f"  {rep}", flush=True)
-    assert rep["unique_experts"] > 200
+    mf.close()
 
 
 # ---- determinism, races, streams, capture ---------------------------------------------
 
-def test_run_to_run_and_poisoned_workspace():
+@pytest.mark.parametrize("T", [8, 32])
+def test_run_to_run_and_poisoned_workspace(T):
     dev = device()
-    shape, seed, T = synth.DECODE_BF16, 2, 8
+    shape, seed = synth.DECODE_BF16, 2
     dl, _ = _decode_layer(shape, seed)
     x = synth.make_tokens(shape, T, seed, stream=T).to(dev)
     for m in MODES:
@@ -136,11 +189,12 @@ def test_run_to_run_and_poisoned_workspace():
         mf.close()
 
 
+@pytest.mark.parametrize("T", [8, 32])
 @pytest.mark.parametrize("hook", ["delay_aux", "delay_main"])
-def test_stream_order_with_injected_delay(hook):
+def test_stream_order_with_injected_delay(hook, T):
     """A spin at the head of one branch must not change a single bit."""
     dev = device()
-    shape, seed, T = synth.DECODE_BF16, 2, 8
+    shape, seed = synth.DECODE_BF16, 2
     dl, _ = _decode_layer(shape, seed)
     x = synth.make_tokens(shape, T, seed, stream=T).to(dev)
     base = run_gpu(_plan(shape, T, "seq"), dl, x)["out"]
@@ -150,10 +204,11 @@ def test_stream_order_with_injected_delay(hook):
         assert torch.equal(run_gpu(mf, dl, x)["out"], base)
 
 
+@pytest.mark.parametrize("T", [8, 32])
 @pytest.mark.parametrize("mode", list(MODES))
-def test_graph_capture_and_replay(mode):
+def test_graph_capture_and_replay(mode, T):
     dev = device()
-    shape, seed, T = synth.DECODE_BF16, 2, 8
+    shape, seed = synth.DECODE_BF16, 2
     dl, _ = _decode_layer(shape, seed)
     mf = _plan(shape, T, mode)
     ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
@@ -216,12 +271,25 @@ def test_max_tokens_256(orc):
     compare(orc, layer, x, got, tol_for(shape))
 
 
-def test_power_of_two_homogeneity():
+def test_max_tokens_256_gemm(orc):
     dev = device()
-    shape = synth.LayerShape(256, 16, 4, 128, 96, "bf16", "bf16")
+    shape = synth.LayerShape(128, 16, 2, 256, 128, "bf16", "bf16")
+    layer = synth.make_layer(shape, 16)
+    x = synth.make_tokens(shape, 256, 16)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=256)
+    got = run_gpu(mf, synth.layer_to(layer, dev), x.to(dev))
+    compare(orc, layer, x, got, tol_for(shape))
+
+
+@pytest.mark.parametrize("regime", [ffn.FORCE_MATVEC, ffn.FORCE_GEMM])
+def test_power_of_two_homogeneity(regime):
+    """Doubling the down weights doubles every output exactly (in both regimes
+    the activation feeding the down product does not depend on them)."""
+    dev = device()
+    shape = synth.LayerShape(256, 16, 4, 128, 128, "bf16", "bf16")
     layer = synth.make_layer(shape, 13)
     x = synth.make_tokens(shape, 5, 13).to(dev)
-    mf = ffn.MoeFfn.for_shape(shape, max_tokens=5)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=5, flags=regime)
     base = run_gpu(mf, synth.layer_to(layer, dev), x)["out"]
     doubled = dict(layer)
     doubled["down"] = (layer["down"].float() * 2).to(torch.bfloat16)
