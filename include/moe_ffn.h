@@ -25,9 +25,11 @@
  * Ownership: the caller owns every tensor, the workspace and the stream; the
  * library borrows them for the duration of the enqueued work (same page,
  * section "Backend services": borrowed device and stream, ordered with the
- * caller's work).  The plan owns a second HIP stream and two events, created
- * lazily by the first forward, which therefore must not run under stream
- * capture.
+ * caller's work).  The plan owns a second HIP stream, two events and about
+ * 1 KiB of device memory (arrival counters of the routing step, zero between
+ * calls),
+ * created lazily by the first forward, which therefore must not run under
+ * stream capture.
  *
  * Threading: a plan serialises nothing.  Two forwards of one plan must not
  * run concurrently (they share the plan's stream and usually the workspace).
@@ -168,8 +170,10 @@ typedef struct moe_ffn_plan_info {
 
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
-    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit) */
-    MOE_FFN_K_ROUTE = 1,        /* softmax, top-k, renormalisation, bucketing, job records */
+    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit); for batches above
+                                   16 tokens also the routing, in the same launch */
+    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) for 5..16
+                                   tokens; up to 4 tokens the routed gate/up launch routes */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
     MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */

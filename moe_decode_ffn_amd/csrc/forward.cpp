@@ -2,7 +2,9 @@
 //
 // Kernels of one forward:
 //   router  logits of E router rows and of the shared-gate vector
-//   route   softmax, top-k, renormalisation, bucketing, job records
+//   routing top-k, renormalised weights, bucketing, job records: in every
+//           routed gate/up workgroup (up to 4 tokens), in k_route (mat-vec
+//           regime up to 16 tokens) or in the router launch's tail (above)
 //   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
 //   down    y = down h per pair [+ S for the shared expert]
 //   join    out = sum_j w_j y_j + s * S
@@ -84,6 +86,9 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
         return hip_fail(e, "hipEventCreateWithFlags");
     if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "hipEventCreateWithFlags");
+    const size_t tb = kTicketCount * sizeof(unsigned);
+    if ((e = hipMalloc(&P->tickets, tb)) != hipSuccess) return hip_fail(e, "hipMalloc");
+    if ((e = hipMemsetAsync(P->tickets, 0, tb, stream)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
     if ((e = hipDeviceGetAttribute(&P->cu_count, hipDeviceAttributeMultiprocessorCount, P->d.device)) != hipSuccess)
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
@@ -200,17 +205,19 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.x_bf16 = d.x_dtype == MOE_FFN_BF16;
     rp.T = Ti; rp.H = (int)H; rp.E = (int)E;
     rp.router = t->w_router; rp.gate_vec = t->gate_vec; rp.logits = logits;
-    rp.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
+    // tokens per router workgroup column: 4 for small batches, so that the last
+    // workgroup of each column ranks one token per wave; 8 above
+    rp.tok_tile = std::max(1, std::min(Ti <= 16 ? 4 : 8, (int)(kStageBytes / (H * xb))));
     const int r_rows = router_rows_per_wg(P->map_router);
     const int r_grid = (int)((E + 1 + r_rows - 1) / r_rows);
     const int r_tiles = (Ti + rp.tok_tile - 1) / rp.tok_tile;
 
-    RouteParams qp{};
-    qp.logits = logits; qp.T = Ti; qp.E = (int)E; qp.k = (int)k;
-    qp.ids = ids; qp.wts = wts; qp.gate_s = gate_s; qp.records = records; qp.n_unique = n_unique;
-    qp.pairs = pairs; qp.pos_expert = pos_expert;
-    qp.dbg_ids = t->dbg_topk_ids; qp.dbg_w = t->dbg_topk_weights;
-    qp.dbg_logits = t->dbg_logits; qp.dbg_gate = t->dbg_shared_gate;
+    rp.k = (int)k;
+    rp.ids = ids; rp.wts = wts; rp.gate_s = gate_s; rp.records = records; rp.n_unique = n_unique;
+    rp.pairs = pairs; rp.pos_expert = pos_expert;
+    rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
+    rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
+    rp.tickets = P->tickets;
 
     GateUpParams gp{};
     gp.x = t->x; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
@@ -221,6 +228,24 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gp.records = records; gp.n_unique = n_unique; gp.pairs = pairs; gp.h = h;
     gp.swg = (const uint8_t *)t->sh_gate; gp.swu = (const uint8_t *)t->sh_up;
     gp.ssg = t->sh_gate_scale; gp.ssu = t->sh_up_scale; gp.Is = (int)Is; gp.hs = sh_h;
+    // small batches: every routed gate/up workgroup ranks and buckets the batch from
+    // the logits (no routing step between the router and the experts); larger
+    // ones: the router launch's last workgroups do it once
+    gp.logits = logits; gp.ids = ids; gp.wts = wts; gp.gate_s = gate_s; gp.pos_expert = pos_expert;
+    gp.dbg_ids = t->dbg_topk_ids; gp.dbg_w = t->dbg_topk_weights;
+    gp.dbg_logits = t->dbg_logits; gp.dbg_gate = t->dbg_shared_gate;
+    {
+        GateUpParams q = gp;
+        q.routed = 1;
+        q.route_here = 1;
+        gp.route_here = !gemm && Ti <= kRouteInGateUpMax &&
+                        gate_up_lds_bytes(q, (int)xb) <= kLdsLimit ? 1 : 0;
+        gp.route_lds_off = gate_up_route_lds_off(q, (int)xb);
+    }
+    // else a routing launch of its own (one wave per token) or the router's tail
+    const bool route_kernel = !gp.route_here && !gemm && Ti <= kRouteKernelMax &&
+                              route_kernel_lds_bytes(Ti, (int)k, (int)E) <= kLdsLimit;
+    rp.route_tail = gp.route_here || route_kernel ? 0 : 1;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
     gp.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
     const int gu_tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
@@ -242,8 +267,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gg.Is = (int)Is; gg.records = records; gg.n_unique = n_unique; gg.pairs = pairs;
     gg.hb = (uint16_t *)h; gg.shb = (uint16_t *)sh_h; gg.y = y; gg.S = sh_S;
     const int gg_rows = gg_rows_per_job();
-    // tokens per pass of a shared-expert job: 16, 32 or 64 (routed buckets are small: 16)
-    const int nt_shared = Ti <= 16 ? 1 : Ti <= 32 ? 2 : 4;
+    // 16 tokens per MFMA pass; the shared expert's tokens are split into blocks of 16
+    const int gg_nt = 1;
+    const int gg_tb = (Ti + 16 * gg_nt - 1) / (16 * gg_nt);
     auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
 
     JoinParams jp{};
@@ -257,8 +283,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     auto run_router = [&](hipStream_t s) {
         hipError_t e1 = timed(P, MOE_FFN_K_ROUTER, s,
                               [&] { return launch_router(rp, P->map_router, r_grid, r_tiles, s); });
-        if (e1 != hipSuccess) return e1;
-        return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(qp, s); });
+        if (e1 != hipSuccess || !route_kernel) return e1;
+        return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(rp, s); });
     };
     // grid of a grid-stride expert launch: its jobs, capped at the resident workgroups
     auto expert_grid = [&](int jobs, int occ) { return std::max(1, std::min(jobs, occ * P->cu_count)); };
@@ -289,8 +315,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         g.routed = routed ? 1 : 0;
         g.tiles_routed = (int)((I + gg_rows - 1) / gg_rows);
         g.tiles_shared = shared ? (int)((Is + gg_rows - 1) / gg_rows) : 0;
-        const int nt = routed ? 1 : nt_shared;
-        const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
+        const int nt = gg_nt;
+        const int jobs = g.tiles_shared * gg_tb + (routed ? max_used * g.tiles_routed : 0);
         const int kid = routed ? MOE_FFN_K_GG_GATE_UP : MOE_FFN_K_SH_GATE_UP;
         return timed(P, kid, s, [&] {
             return launch_gg_gate_up(g, nt, expert_grid(jobs, P->occ_gg_gu[nt_index(nt)]), s);
@@ -302,8 +328,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         g.routed = routed ? 1 : 0;
         g.tiles_routed = (int)((H + gg_rows - 1) / gg_rows);
         g.tiles_shared = shared ? g.tiles_routed : 0;
-        const int nt = routed ? 1 : nt_shared;
-        const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
+        const int nt = gg_nt;
+        const int jobs = g.tiles_shared * gg_tb + (routed ? max_used * g.tiles_routed : 0);
         const int kid = routed ? MOE_FFN_K_GG_DOWN : MOE_FFN_K_SH_DOWN;
         return timed(P, kid, s, [&] {
             return launch_gg_down(g, nt, expert_grid(jobs, P->occ_gg_d[nt_index(nt)]), s);
@@ -370,6 +396,7 @@ void moe_ffn_destroy(moe_ffn_plan_t P) {
     if (P->ev_fork) hipEventDestroy(P->ev_fork);
     if (P->ev_join) hipEventDestroy(P->ev_join);
     if (P->aux) hipStreamDestroy(P->aux);
+    if (P->tickets) hipFree(P->tickets);
     delete P;
 }
 

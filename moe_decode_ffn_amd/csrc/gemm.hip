@@ -6,6 +6,9 @@
 //
 // Tiling: a wave owns 16 weight rows (the MFMA M side) and up to 16*NT tokens
 // of the job's expert (N side, 16 per tile, zero-padded), K in chunks of 128.
+// A job is 64 rows (four waves) of one expert; a routed job walks its whole
+// bucket in passes of 16*NT tokens, a shared-expert job owns one block of
+// 16*NT tokens, so the shared expert spreads over (row tiles x token blocks).
 // v_mfma_f32_16x16x32_bf16 takes 8 bf16 of A and 8 of B per lane from the same
 // K slot (lane group g = lane/16); a sum over K does not care which K slot
 // holds which element as long as A and B agree.  So in MFMA step s of a
@@ -44,22 +47,30 @@ struct GGJob {
     bool valid, routed;
     const uint8_t *W0, *W1;
     int K, rows, tile, ntok;
+    int tok0;            // shared expert: first token of the job's block
     const int *rec;
 };
 
-__device__ __forceinline__ GGJob gg_decode(int j, int tiles_shared, int tiles_routed, int nu,
-                                           const int *records, int E, int npairs, const uint8_t *rW0,
-                                           const uint8_t *rW1, int rrows, int rK, const uint8_t *sW0,
-                                           const uint8_t *sW1, int srows, int sK, int T) {
+// Jobs: the shared expert's (row tile, token block) pairs first, token blocks
+// of tb_len tokens, then tiles_routed row tiles per used expert.
+__device__ __forceinline__ GGJob gg_decode(int j, int tiles_shared, int tb_len, int tiles_routed,
+                                           int nu, const int *records, int E, int npairs,
+                                           const uint8_t *rW0, const uint8_t *rW1, int rrows, int rK,
+                                           const uint8_t *sW0, const uint8_t *sW1, int srows, int sK,
+                                           int T) {
     GGJob jb{};
     jb.valid = false;
-    if (j < tiles_shared) {
+    const int n_tb = (T + tb_len - 1) / tb_len;
+    if (j < tiles_shared * n_tb) {
+        const int tb = j / tiles_shared;
         jb.valid = true; jb.routed = false;
-        jb.W0 = sW0; jb.W1 = sW1; jb.K = sK; jb.rows = srows; jb.tile = j; jb.ntok = T;
+        jb.W0 = sW0; jb.W1 = sW1; jb.K = sK; jb.rows = srows; jb.tile = j - tb * tiles_shared;
+        jb.tok0 = tb * tb_len;
+        jb.ntok = min(tb_len, T - jb.tok0);
         jb.rec = nullptr;
         return jb;
     }
-    j -= tiles_shared;
+    j -= tiles_shared * n_tb;
     const int slot = j / tiles_routed;
     if (slot >= nu) return jb;
     const int *rec = records + (size_t)slot * kRecInts;
@@ -69,7 +80,8 @@ __device__ __forceinline__ GGJob gg_decode(int j, int tiles_shared, int tiles_ro
     const size_t m0 = (size_t)e * rrows * rK * 2;
     jb.W0 = rW0 + m0;
     jb.W1 = rW1 ? rW1 + m0 : nullptr;
-    jb.K = rK; jb.rows = rrows; jb.tile = j - slot * tiles_routed; jb.ntok = cnt; jb.rec = rec;
+    jb.K = rK; jb.rows = rrows; jb.tile = j - slot * tiles_routed; jb.ntok = cnt; jb.tok0 = 0;
+    jb.rec = rec;
     return jb;
 }
 
@@ -93,10 +105,10 @@ __global__ __launch_bounds__(256) void k_gg_gate_up(GGParams p) {
     const int T = p.T, k = p.k, npairs = T * k;
     int nu = p.routed ? *p.n_unique : 0;
     nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
-    const int J = p.tiles_shared + nu * p.tiles_routed;
+    const int J = p.tiles_shared * ((T + 16 * NT - 1) / (16 * NT)) + nu * p.tiles_routed;
     for (int j = blockIdx.x; j < J; j += gridDim.x) {
-        const GGJob jb = gg_decode(j, p.tiles_shared, p.tiles_routed, nu, p.records, p.E, npairs,
-                                   p.w0, p.w1, p.I, p.H, p.sw0, p.sw1, p.Is, p.H, T);
+        const GGJob jb = gg_decode(j, p.tiles_shared, 16 * NT, p.tiles_routed, nu, p.records, p.E,
+                                   npairs, p.w0, p.w1, p.I, p.H, p.sw0, p.sw1, p.Is, p.H, T);
         if (!jb.valid) continue;
         const int row = jb.tile * kGGRows + wave * 16 + ri;  // A row of this lane
         const bool rok = row < jb.rows;
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(256) void k_gg_gate_up(GGParams p) {
                         bok[n] = pr >= 0 && pr < npairs;
                         tok = bok[n] ? pr / k : 0;
                     } else {
-                        tok = a;
+                        tok = jb.tok0 + a;
                     }
                 }
                 brow[n] = (const uint8_t *)p.x + (size_t)tok * p.H * 2;
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void k_gg_gate_up(GGParams p) {
             for (int n = 0; n < NT; ++n) {
                 const int a = t0 + 16 * n + ri;
                 if (a >= jb.ntok) continue;
-                int orow = a;
+                int orow = jb.tok0 + a;
                 if (jb.routed) {
                     orow = gg_pair(jb.rec, p.pairs, a);
                     if (orow < 0 || orow >= npairs) continue;
@@ -192,10 +204,10 @@ __global__ __launch_bounds__(256) void k_gg_down(GGParams p) {
     const int T = p.T, k = p.k, npairs = T * k, H = p.H;
     int nu = p.routed ? *p.n_unique : 0;
     nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
-    const int J = p.tiles_shared + nu * p.tiles_routed;
+    const int J = p.tiles_shared * ((T + 16 * NT - 1) / (16 * NT)) + nu * p.tiles_routed;
     for (int j = blockIdx.x; j < J; j += gridDim.x) {
-        const GGJob jb = gg_decode(j, p.tiles_shared, p.tiles_routed, nu, p.records, p.E, npairs,
-                                   p.w0, nullptr, H, p.I, p.sw0, nullptr, H, p.Is, T);
+        const GGJob jb = gg_decode(j, p.tiles_shared, 16 * NT, p.tiles_routed, nu, p.records, p.E,
+                                   npairs, p.w0, nullptr, H, p.I, p.sw0, nullptr, H, p.Is, T);
         if (!jb.valid) continue;
         const int row = jb.tile * kGGRows + wave * 16 + ri;
         const bool rok = row < jb.rows;
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(256) void k_gg_down(GGParams p) {
                         bok[n] = pr >= 0 && pr < npairs;
                         src = bok[n] ? pr : 0;
                     } else {
-                        src = a;
+                        src = jb.tok0 + a;
                     }
                 }
                 brow[n] = hbase + (size_t)src * rb;
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256) void k_gg_down(GGParams p) {
             for (int n = 0; n < NT; ++n) {
                 const int a = t0 + 16 * n + ri;
                 if (a >= jb.ntok) continue;
-                int orow = a;
+                int orow = jb.tok0 + a;
                 if (jb.routed) {
                     orow = gg_pair(jb.rec, p.pairs, a);
                     if (orow < 0 || orow >= npairs) continue;

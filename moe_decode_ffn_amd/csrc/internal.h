@@ -18,6 +18,10 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
 constexpr int kDefaultMatvecMax = 16;
+constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
+constexpr int kRouteKernelMax = 16;   // up to this batch (mat-vec regime) k_route routes it
+// arrival counters in plan memory: one per router token tile, one across tiles
+constexpr int kTicketCount = kMaxTokens + 1;
 constexpr size_t kWsAlign = 256;
 constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
 constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
@@ -76,6 +80,7 @@ struct moe_ffn_plan_s {
     bool ready = false;
     hipStream_t aux = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    unsigned *tickets = nullptr;  // device arrival counters of the router's routing tail
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
@@ -98,16 +103,12 @@ constexpr int kRecPairs = kRecInts - 4;
 struct RouterParams {
     const void *x;
     int x_bf16;
-    int T, H, E;
+    int T, H, E, k;
     const float *router;    // [E][H]
     const float *gate_vec;  // [H] (acts as row E)
     float *logits;          // [T][E+1]
     int tok_tile;           // tokens per workgroup column
-};
-
-struct RouteParams {
-    const float *logits;    // [T][E+1]
-    int T, E, k;
+    // routing outputs (written by the last workgroup of each token tile / of the launch)
     int *ids;               // [T*k]
     float *wts;             // [T*k]
     float *gate_s;          // [T]
@@ -117,6 +118,8 @@ struct RouteParams {
     int *pos_expert;        // [T*k]
     int32_t *dbg_ids;
     float *dbg_w, *dbg_logits, *dbg_gate;
+    unsigned *tickets;      // plan memory: [kMaxTokens] per token tile + [1] across tiles, zero between calls
+    int route_tail;         // 1: the launch also ranks and buckets (else k_route or the gate/up launch)
 };
 
 struct GateUpParams {
@@ -140,6 +143,16 @@ struct GateUpParams {
     int Is;
     float *hs;                     // [T][Is]
     int tiles_shared;              // jobs of the shared expert (0 = not in this launch)
+    // routing in every workgroup (small batches; routed launches only)
+    int route_here;                // 1: rank and bucket the batch from the logits here
+    int route_lds_off;             // byte offset of the routing area in dynamic LDS
+    const float *logits;           // [T][E+1]
+    int *ids;                      // global tables, written by workgroup 0
+    float *wts;
+    float *gate_s;
+    int *pos_expert;
+    int32_t *dbg_ids;
+    float *dbg_w, *dbg_logits, *dbg_gate;
 };
 
 struct DownParams {
@@ -191,7 +204,6 @@ struct JoinParams {
 // ---- launchers (kernel files) -------------------------------------------
 hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
                          hipStream_t s);
-hipError_t launch_route(const RouteParams &p, hipStream_t s);
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_join(const JoinParams &p, hipStream_t s);
@@ -206,8 +218,11 @@ int router_rows_per_wg(const RowMap &m);
 int gate_up_rows_per_wg(int wkind, const RowMap &m);
 int down_rows_per_wg(int wkind, const RowMap &m);
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);
+int gate_up_route_lds_off(const GateUpParams &p, int xbytes);
 size_t router_lds_bytes(const RouterParams &p);
 size_t route_lds_bytes(int T, int k, int E);
+size_t route_kernel_lds_bytes(int T, int k, int E);
+hipError_t launch_route(const RouterParams &p, hipStream_t s);
 int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds);
 
 // ---- planner helpers (plan.cpp) ---------------------------------------------

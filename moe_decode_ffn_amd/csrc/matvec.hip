@@ -19,6 +19,7 @@
 // dequantised in registers).
 #include "device.h"
 #include "internal.h"
+#include "routing.h"
 
 namespace moeffn {
 
@@ -254,20 +255,51 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     const int n_chunks = (int)(row_bytes<WK>(H) / 16);
     const int npairs = T * k;
     const size_t xrow = (size_t)H * XB;
-    int nu = p.routed ? *p.n_unique : 0;
-    nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
-    const int J = p.tiles_shared + nu * p.tiles_routed;
+    // routing tables: global (routed by the router launch) or this workgroup's LDS
+    const int *recs = p.records, *prs = p.pairs;
+    int nu = 0;
     int j = blockIdx.x;
-    if (j >= J) return;
-
     auto decode = [&](int jj) {
-        return decode_job<WK>(jj, p.tiles_shared, p.tiles_routed, nu, p.records, p.E, npairs, p.wg, p.wu,
+        return decode_job<WK>(jj, p.tiles_shared, p.tiles_routed, nu, recs, p.E, npairs, p.wg, p.wu,
                               p.sg, p.su, p.I, H, p.swg, p.swu, p.ssg, p.ssu, p.Is, H, T);
     };
     uint4 ag[RPW][NC], au[RPW][NC], bg[RPW][NC], bu[RPW][NC];
     float asg[RPW][NC], asu[RPW][NC], bsg[RPW][NC], bsu[RPW][NC];
-    Job ja = decode(j), jb{};
-    load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+    Job ja{}, jb{};
+    bool loaded = false;
+    const bool route_here = p.routed && p.route_here;
+    if (!route_here) {
+        nu = p.routed ? *p.n_unique : 0;
+        nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
+        if (j >= p.tiles_shared + nu * p.tiles_routed) return;
+    }
+    if (!route_here || j < p.tiles_shared) {  // a shared-expert job needs no routing
+        ja = decode(j);
+        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+        loaded = true;
+    }
+    if (route_here) {
+        // every workgroup ranks and buckets the whole batch; workgroup 0 publishes
+        uint8_t *area = lds + p.route_lds_off;
+        const RouteLds L = route_lds_layout(T, k, p.E, kWaves, true);
+        const bool pub = blockIdx.x == 0;
+        RouteGlobal g{};
+        if (pub) g = RouteGlobal{p.ids, p.wts, p.gate_s, const_cast<int *>(p.records),
+                                 const_cast<int *>(p.n_unique), const_cast<int *>(p.pairs), p.pos_expert,
+                                 p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
+        rank_tokens(p.logits, 0, T, p.E, k, area, L, g, false);
+        nu = bucket_tokens(T, k, p.E, area, L, g);
+        nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
+        recs = reinterpret_cast<const int *>(area + L.records);
+        prs = reinterpret_cast<const int *>(area + L.pairs);
+    }
+    const int J = p.tiles_shared + nu * p.tiles_routed;
+    if (j >= J) return;
+    if (!loaded) {
+        ja = decode(j);
+        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+    }
+    // tokens staged once, their loads in flight together with the first job's weights
     if (p.x_resident) {
         const int n16 = (int)(T * xrow / 16);
         for (int i = tid; i < n16; i += 256)
@@ -290,7 +322,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                     const int a = i / xr16, c = i - a * xr16;
                     int tok = t0 + a;
                     if (job.routed) {
-                        const int pr = job_pair(job.rec, p.pairs, t0 + a);
+                        const int pr = job_pair(job.rec, prs, t0 + a);
                         tok = (pr >= 0 && pr < npairs) ? pr / k : 0;
                     }
                     reinterpret_cast<uint4 *>(lds)[i] =
@@ -301,7 +333,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
             for (int a = 0; a < nt; ++a) {
                 int orow = t0 + a, tok = t0 + a;
                 if (job.routed) {
-                    orow = job_pair(job.rec, p.pairs, t0 + a);
+                    orow = job_pair(job.rec, prs, t0 + a);
                     tok = orow / k;
                 }
                 const bool ook = orow >= 0 && orow < (job.routed ? npairs : T);
@@ -443,7 +475,6 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
             }
         }
     };
-
     for (;;) {
         const int j2 = j + gridDim.x;
         if (j2 < J) {
@@ -501,7 +532,13 @@ __global__ __launch_bounds__(256) void k_join(JoinParams p) {
 
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes) {
     const int toks = p.x_resident ? p.T : p.tok_per_pass;
-    return (size_t)toks * p.H * xbytes;
+    const size_t stage = ((size_t)toks * p.H * xbytes + 15) & ~(size_t)15;
+    return stage + (p.routed && p.route_here ? route_lds_layout(p.T, p.k, p.E, kWaves, true).bytes : 0);
+}
+
+int gate_up_route_lds_off(const GateUpParams &p, int xbytes) {
+    const int toks = p.x_resident ? p.T : p.tok_per_pass;
+    return (int)(((size_t)toks * p.H * xbytes + 15) & ~(size_t)15);
 }
 
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s) {

@@ -1,14 +1,18 @@
 // router.hip -- router GEMV (fp32 rows; row E is the shared-expert gate
-// vector, so its logit is sigma's argument) and the routing kernel.
+// vector, so its logit is sigma's argument) with the routing folded into the
+// same launch.
 //
-// k_router: logits [T][E+1]; workgroups tile (rows x tokens), no cross-
-//   workgroup communication.
-// k_route: one workgroup of 1024 threads ranks every token (one wave per
-//   token, routing.h), buckets the (token, slot) pairs by expert and writes
-//   the tables the expert kernels read: ids and weights per slot, the gate
-//   value per token, and one 64-byte job record per used expert
-//   (expert, first position, count, 0, first 12 pair ids) so an expert
-//   workgroup learns everything about its job from one scalar load.
+// Workgroups tile (rows x tokens).  Where the routing runs depends on the
+// batch: in every gate/up workgroup (a few tokens), in k_route (one wave per
+// token, mid-size batches), or in this launch's tail (larger batches): after
+// writing its logits a workgroup takes a ticket for its token tile; the last one to arrive for a tile ranks that
+// tile's tokens (one wave per token, routing.h): ids, renormalised weights and
+// the shared-expert gate.  With several token tiles a second ticket elects
+// the last tile, which buckets every (token, slot) pair by expert and writes
+// the tables the expert kernels read: one 64-byte job record per used expert
+// (expert, first position, count, 0, first 12 pair ids) so an expert
+// workgroup learns everything about its job from one scalar load.  Tickets are
+// counters in plan memory that the last arriver puts back to zero.
 #include "device.h"
 #include "internal.h"
 #include "routing.h"
@@ -16,7 +20,6 @@
 namespace moeffn {
 
 constexpr int kRouterWaves = 4;
-constexpr int kRouteThreads = 1024;
 
 int router_rows_per_wg(const RowMap &m) { return kRouterWaves * (64 / m.lpr); }
 
@@ -70,57 +73,54 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         acc = seg_sum<LPR>(acc);
         if (valid && sl == 0) p.logits[(size_t)(t0 + i) * (E + 1) + row] = acc;
     }
+
+    // ---- routing tail ----
+    if (!p.route_tail) return;
+    if (!last_arrival(p.tickets + blockIdx.y, gridDim.x)) return;
+    const int T = p.T, k = p.k;
+    const RouteLds L = route_lds_layout(T, k, E, kRouterWaves, false);
+    const bool one_tile = gridDim.y == 1;
+    const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
+                        p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
+    rank_tokens(p.logits, t0, t0 + nt, E, k, lds, L, g, !one_tile);
+    if (!one_tile) {
+        if (!last_arrival(p.tickets + kMaxTokens, gridDim.y)) return;
+        int *ids = reinterpret_cast<int *>(lds + L.ids);
+        for (int i = tid; i < T * k; i += blockDim.x) ids[i] = p.ids[i];
+    }
+    bucket_tokens(T, k, E, lds, L, g);
 }
 
-__global__ __launch_bounds__(kRouteThreads) void k_route(RouteParams p) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-    const int T = p.T, E = p.E, k = p.k, NP = T * k;
-    int *r_ids = reinterpret_cast<int *>(lds);       // [NP]
-    int *r_pairs = r_ids + NP;                       // [NP]
-    int *r_pose = r_pairs + NP;                      // [NP]
-    int *r_nu = r_pose + NP;                         // [4]
-    int4 *r_slots = reinterpret_cast<int4 *>(lds + (((size_t)(3 * NP + 4) * 4 + 15) & ~(size_t)15));
-    uint32_t *scratch = reinterpret_cast<uint32_t *>(r_slots + (E < NP ? E : NP));
+size_t route_lds_bytes(int T, int k, int E) { return route_lds_layout(T, k, E, kRouterWaves, false).bytes; }
 
-    for (int t = wave; t < T; t += nw) {
-        RouteOut o{r_ids + t * k, p.wts + t * k, p.gate_s + t,
-                   p.dbg_ids ? p.dbg_ids + t * k : nullptr, p.dbg_w ? p.dbg_w + t * k : nullptr,
-                   p.dbg_gate ? p.dbg_gate + t : nullptr,
-                   p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
-        route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
-    }
-    __syncthreads();
-    bucket_pairs(r_ids, T, k, E, scratch, r_slots, r_pairs, r_pose, r_nu);
-    __syncthreads();
-    const int nu = *r_nu;
-    for (int i = tid; i < NP; i += blockDim.x) {
-        p.ids[i] = r_ids[i];
-        p.pairs[i] = r_pairs[i];
-        p.pos_expert[i] = r_pose[i];
-    }
-    for (int i = tid; i < nu * kRecInts; i += blockDim.x) {
-        const int u = i / kRecInts, f = i - u * kRecInts;
-        const int4 s = r_slots[u];
-        int v;
-        if (f == 0) v = s.x;
-        else if (f == 1) v = s.y;
-        else if (f == 2) v = s.z;
-        else if (f == 3) v = 0;
-        else v = (f - 4 < s.z) ? r_pairs[s.y + f - 4] : -1;
-        p.records[i] = v;
-    }
-    if (tid == 0) *p.n_unique = nu;
+// k_route: one workgroup, one wave per token (up to 16), ranks the batch and
+// buckets it (mid-size batches, between in-gate/up routing and the router tail).
+__global__ __launch_bounds__(1024) void k_route(RouterParams p) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const RouteLds L = route_lds_layout(p.T, p.k, p.E, blockDim.x >> 6, false);
+    const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
+                        p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
+    rank_tokens(p.logits, 0, p.T, p.E, p.k, lds, L, g, false);
+    bucket_tokens(p.T, p.k, p.E, lds, L, g);
+}
+
+int route_kernel_waves(int T) { return T < 4 ? 4 : T > 16 ? 16 : T; }
+
+size_t route_kernel_lds_bytes(int T, int k, int E) {
+    return route_lds_layout(T, k, E, route_kernel_waves(T), false).bytes;
+}
+
+hipError_t launch_route(const RouterParams &p, hipStream_t s) {
+    const size_t lds = route_kernel_lds_bytes(p.T, p.k, p.E);
+    if (lds > kLdsLimit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * route_kernel_waves(p.T)), lds, s, p);
+    return hipGetLastError();
 }
 
 size_t router_lds_bytes(const RouterParams &p) {
-    return (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
-}
-
-size_t route_lds_bytes(int T, int k, int E) {
-    const int np = T * k;
-    return (((size_t)(3 * np + 4) * 4 + 15) & ~(size_t)15) + (size_t)(E < np ? E : np) * 16 +
-           (size_t)bucket_scratch_ints(E, T) * 4;
+    const size_t stage = (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
+    const size_t tail = p.route_tail ? route_lds_bytes(p.T, p.k, p.E) : 0;
+    return stage > tail ? stage : tail;
 }
 
 template <int LPR, int NC>
@@ -150,15 +150,6 @@ hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, 
     case 6432: return launch_router_t<64, 32>(p, grid_rows, grid_tiles, s);
     default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_route(const RouteParams &p, hipStream_t s) {
-    const size_t lds = route_lds_bytes(p.T, p.k, p.E);
-    if (lds > kLdsLimit) return hipErrorInvalidValue;
-    // one wave per token up to 16 waves
-    const int waves = p.T < 16 ? (p.T < 4 ? 4 : p.T) : 16;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * waves), lds, s, p);
-    return hipGetLastError();
 }
 
 // ---- bounded delay (test hook) ------------------------------------------------------

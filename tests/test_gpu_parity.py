@@ -171,6 +171,61 @@ def test_decode_bf16_t128(orc):
     mf.close()
 
 
+def test_many_pairs_top16(orc):
+    """256 tokens x top-16 over 64 experts: 4096 pairs, big buckets."""
+    dev = device()
+    shape = synth.LayerShape(128, 64, 16, 64, 64, "bf16", "bf16")
+    layer = synth.make_layer(shape, 25)
+    x = synth.make_tokens(shape, 256, 25)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=256, flags=ffn.SHARED_FUSED)
+    got = run_gpu(mf, synth.layer_to(layer, dev), x.to(dev))
+    compare(orc, layer, x, got, tol_for(shape))
+
+
+# ---- exact ties in the routing ----------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 9])
+def test_exact_ties_go_to_the_lower_index(orc, T):
+    """Duplicated router rows give bit-equal logits; the picks among them
+    follow the expert index (and the oracle's fp64 ranking, tie for tie)."""
+    dev = device()
+    shape = synth.LayerShape(128, 16, 4, 64, 64, "bf16", "bf16")
+    layer = dict(synth.make_layer(shape, 26))
+    r = layer["router"].clone()
+    r[9] = r[2]
+    r[12] = r[4]
+    r[5] = r[4]
+    r[[2, 4, 5, 9, 12]] *= 4.0  # large enough to be picked for most tokens
+    layer["router"] = r.contiguous()
+    x = synth.make_tokens(shape, T, 26)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
+    got = run_gpu(mf, synth.layer_to(layer, dev), x.to(dev))
+    ref = orc.forward(oracle_layer(layer), oracle_tokens(x))
+    assert np.array_equal(got["ids"].numpy(), ref["ids"]), (got["ids"], ref["ids"])
+    ids = got["ids"].numpy()
+    for t in range(T):
+        pos = {int(e): j for j, e in enumerate(ids[t])}
+        for lo, hi in ((2, 9), (4, 5), (5, 12)):
+            if lo in pos and hi in pos:
+                assert pos[lo] < pos[hi], f"token {t}: expert {lo} must precede {hi}"
+            assert not (hi in pos and lo not in pos), f"token {t}: {hi} picked without {lo}"
+
+
+def test_all_logits_equal():
+    """A zero router: every logit is +0, so the picks are experts 0..k-1 in
+    order with equal weights, and a zero gate vector gives s = 1/2."""
+    dev = device()
+    shape = synth.LayerShape(128, 16, 4, 64, 64, "bf16", "bf16")
+    layer = dict(synth.make_layer(shape, 27))
+    layer["router"] = torch.zeros_like(layer["router"])
+    layer["gate_vec"] = torch.zeros_like(layer["gate_vec"])
+    x = synth.make_tokens(shape, 3, 27)
+    got = run_gpu(ffn.MoeFfn.for_shape(shape, max_tokens=3), synth.layer_to(layer, dev), x.to(dev))
+    assert torch.equal(got["ids"], torch.arange(4, dtype=torch.int32).repeat(3, 1))
+    assert torch.all((got["weights"] - 0.25).abs() <= 1e-7)
+    assert torch.all(got["gate"] == 0.5)
+
+
 # ---- determinism, races, streams, capture ---------------------------------------------
 
 @pytest.mark.parametrize("T", [8, 32])
