@@ -33,15 +33,6 @@ TOKEN_POOL = 8
 WINDOW_REPEATS = 4
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "moe_decode_ffn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def expert_bytes(shape) -> tuple[int, int]:
     """(gate+up bytes, down bytes) of one expert (or the shared expert) in its storage."""
     H, I = shape.hidden, shape.inter
@@ -61,10 +52,12 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_bf16_t1")
     ap.add_argument("--mode", default="auto", choices=["auto", "aux", "seq", "fused"])
     ap.add_argument("--regime", default="auto", choices=["auto", "matvec", "gemm"])
+    ap.add_argument("--tokens", type=int, default=0, help="override the workload's batch (sweeps)")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--traffic", default=None, help="traffic JSON written from rocprofv3 counters")
+    ap.add_argument("--traffic", default=None,
+                    help="traffic summary from rocprofv3 counters (default profiles/traffic_<workload>.md)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -76,12 +69,13 @@ def main() -> int:
     import torch
 
     from moe_decode_ffn_amd import ffn, synth
+    from moe_decode_ffn_amd.traffic import kernel_source_hash, read_summary
 
     if args.workload not in synth.WORKLOADS:
         print(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}", file=sys.stderr)
         return 2
     shape, seed, counts = synth.WORKLOADS[args.workload]
-    T = counts[-1]
+    T = args.tokens or counts[-1]
     dev = torch.device("cuda:0")
     mode = {"auto": ffn.SHARED_AUTO, "aux": ffn.SHARED_AUX, "seq": ffn.SHARED_SEQ,
             "fused": ffn.SHARED_FUSED}[args.mode]
@@ -178,11 +172,14 @@ def main() -> int:
     achieved = gu_units * gu_b / (avg_us * 1e-6) / 1e9
     kernels = {k: round(v[0] * 1e3 / v[1], 3) for k, v in prof.items() if v[1]}
 
+    # HBM bytes per launch of the dominant kernel from rocprofv3 counters, valid
+    # only while the kernel sources are the ones the counters were taken on
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        rec = json.load(open(args.traffic))
-        if rec.get("kernel_source_hash") == kernel_source_hash() and rec.get("workload") == args.workload:
-            traffic = rec.get("hbm_bytes_per_launch")
+    rec = read_summary(args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.md"))
+    if (rec and rec.get("kernel_source_hash") == kernel_source_hash()
+            and rec.get("workload") == args.workload and rec.get("shared_mode") == shared_mode
+            and dominant in str(rec.get("kernel", ""))):
+        traffic = rec.get("hbm_bytes_per_launch")
 
     # ---- the oracle on the host cores (a bounded sample of the same workload) ----------------
     cpu = None

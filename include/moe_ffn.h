@@ -85,7 +85,7 @@ typedef enum moe_ffn_dtype {
  * expert forked onto one auxiliary stream and joined at the add, only in the
  * small-batch mat-vec regime, output identical to sequential order).  Every
  * mode gives bit-identical output for the same inputs. */
-#define MOE_FFN_SHARED_AUTO 0x0u   /* FUSED up to matvec_max_tokens, AUX above (moe_ffn_plan_info) */
+#define MOE_FFN_SHARED_AUTO 0x0u   /* FUSED in both regimes (measured fastest; moe_ffn_plan_info) */
 #define MOE_FFN_SHARED_AUX 0x1u    /* second stream of the plan, event fork at entry, event join before the add */
 #define MOE_FFN_SHARED_SEQ 0x2u    /* same kernels, all on the caller's stream, shared branch first */
 #define MOE_FFN_SHARED_FUSED 0x3u  /* shared expert folded into the routed kernels' grids (fewest launches) */
@@ -122,7 +122,7 @@ typedef struct moe_ffn_desc {
     int32_t x_dtype;            /* moe_ffn_dtype of x: F32 or BF16 */
     int32_t weight_dtype;       /* moe_ffn_dtype of every routed and shared FFN matrix */
     uint32_t flags;             /* MOE_FFN_SHARED_*, MOE_FFN_FORCE_*, MOE_FFN_DEBUG_* */
-    int32_t matvec_max_tokens;  /* regime switch; 0 = library default (16) */
+    int32_t matvec_max_tokens;  /* regime switch; 0 = library default (6) */
 } moe_ffn_desc;
 
 /* Device pointers for one forward.  Row-major, contiguous, 16-byte aligned.
@@ -171,9 +171,10 @@ typedef struct moe_ffn_plan_info {
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit); for batches above
-                                   16 tokens also the routing, in the same launch */
-    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) for 5..16
-                                   tokens; up to 4 tokens the routed gate/up launch routes */
+                                   32 tokens also the routing, in the same launch */
+    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) up to 32 tokens,
+                                   except up to 4 tokens in the mat-vec regime, where the routed
+                                   gate/up launch routes */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
     MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */

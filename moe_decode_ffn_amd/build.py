@@ -1,4 +1,5 @@
-"""Builds libmoe_ffn.so for gfx950 in-tree (moe_decode_ffn_amd/lib/).
+"""Builds libmoe_ffn.so for gfx950 in-tree (moe_decode_ffn_amd/lib/), and the
+layer_loop driver (a C-ABI-only program for profiler runs) beside it.
 
     python -m moe_decode_ffn_amd.build
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBRARY = os.path.join(LIBDIR, "libmoe_ffn.so")
+DRIVER_SRC = os.path.join(PKG, "driver", "layer_loop.hip")
+DRIVER = os.path.join(LIBDIR, "layer_loop")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -59,6 +62,18 @@ def build_library(jobs: int | None = None) -> str:
     return LIBRARY
 
 
+def build_driver() -> str:
+    """layer_loop, linked against the in-tree library (found next to it at run time)."""
+    tmp = DRIVER + ".tmp"
+    cmd = [HIPCC, *COMMON, DRIVER_SRC, "-o", tmp, f"-L{LIBDIR}", "-lmoe_ffn", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {DRIVER_SRC}:\n{r.stderr}")
+    os.replace(tmp, DRIVER)
+    return DRIVER
+
+
 if __name__ == "__main__":
     print(build_library())
+    print(build_driver())
     sys.exit(0)

@@ -3,8 +3,8 @@
 // Kernels of one forward:
 //   router  logits of E router rows and of the shared-gate vector
 //   routing top-k, renormalised weights, bucketing, job records: in every
-//           routed gate/up workgroup (up to 4 tokens), in k_route (mat-vec
-//           regime up to 16 tokens) or in the router launch's tail (above)
+//           routed mat-vec gate/up workgroup (up to 4 tokens), in k_route (up
+//           to 32 tokens) or in the router launch's tail (above)
 //   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
 //   down    y = down h per pair [+ S for the shared expert]
 //   join    out = sum_j w_j y_j + s * S
@@ -27,6 +27,10 @@
 #include "internal.h"
 
 using namespace moeffn;
+
+namespace moeffn {
+thread_local LaunchEvents g_launch_events;
+}
 
 namespace {
 
@@ -58,17 +62,22 @@ hipEvent_t pool_event(moe_ffn_plan_s *P) {
     return e;
 }
 
-// Runs `launch` on stream s, bracketed by timing events when profiling.
+// Runs `launch` on stream s; when profiling, the kernel's own dispatch records
+// a pair of timing events (its start and end), so the interval is the
+// kernel's duration without the gaps around it.
 template <class F>
 hipError_t timed(moe_ffn_plan_s *P, int kernel, hipStream_t s, F &&launch) {
     if (!P->profiling) return launch();
     hipEvent_t a = pool_event(P), b = pool_event(P);
     if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, s);
+    g_launch_events = LaunchEvents{a, b};
+    hipError_t e = launch();
+    if (g_launch_events.start) {  // nothing was launched (an empty grid): a zero interval
+        g_launch_events = LaunchEvents{};
+        if (e == hipSuccess) e = hipEventRecord(a, s);
+        if (e == hipSuccess) e = hipEventRecord(b, s);
+    }
     if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(b, s);
     P->prof.push_back({kernel, a, b});
     return e;
 }
@@ -243,7 +252,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         gp.route_lds_off = gate_up_route_lds_off(q, (int)xb);
     }
     // else a routing launch of its own (one wave per token) or the router's tail
-    const bool route_kernel = !gp.route_here && !gemm && Ti <= kRouteKernelMax &&
+    const bool route_kernel = !gp.route_here && Ti <= kRouteKernelMax &&
                               route_kernel_lds_bytes(Ti, (int)k, (int)E) <= kLdsLimit;
     rp.route_tail = gp.route_here || route_kernel ? 0 : 1;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);

@@ -288,17 +288,17 @@ __global__ __launch_bounds__(256) void k_gg_down(GGParams p) {
 
 hipError_t launch_gg_gate_up(const GGParams &p, int nt, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    if (nt <= 1) hipLaunchKernelGGL(k_gg_gate_up<1>, dim3(grid), dim3(256), 0, s, p);
-    else if (nt <= 2) hipLaunchKernelGGL(k_gg_gate_up<2>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(k_gg_gate_up<4>, dim3(grid), dim3(256), 0, s, p);
+    if (nt <= 1) launch_kernel(k_gg_gate_up<1>, dim3(grid), dim3(256), 0, s, p);
+    else if (nt <= 2) launch_kernel(k_gg_gate_up<2>, dim3(grid), dim3(256), 0, s, p);
+    else launch_kernel(k_gg_gate_up<4>, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_gg_down(const GGParams &p, int nt, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    if (nt <= 1) hipLaunchKernelGGL(k_gg_down<1>, dim3(grid), dim3(256), 0, s, p);
-    else if (nt <= 2) hipLaunchKernelGGL(k_gg_down<2>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(k_gg_down<4>, dim3(grid), dim3(256), 0, s, p);
+    if (nt <= 1) launch_kernel(k_gg_down<1>, dim3(grid), dim3(256), 0, s, p);
+    else if (nt <= 2) launch_kernel(k_gg_down<2>, dim3(grid), dim3(256), 0, s, p);
+    else launch_kernel(k_gg_down<4>, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // the kernel files of the MoE decode FFN library (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -17,9 +18,9 @@ constexpr int kMaxTokens = 256;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
-constexpr int kDefaultMatvecMax = 16;
+constexpr int kDefaultMatvecMax = 6;  // measured crossover of the mat-vec and grouped-GEMM kernels
 constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
-constexpr int kRouteKernelMax = 16;   // up to this batch (mat-vec regime) k_route routes it
+constexpr int kRouteKernelMax = 32;   // up to this batch k_route routes it (else the router tail)
 // arrival counters in plan memory: one per router token tile, one across tiles
 constexpr int kTicketCount = kMaxTokens + 1;
 constexpr size_t kWsAlign = 256;
@@ -200,6 +201,25 @@ struct JoinParams {
     const float *S;      // [T][H]
     float *out;          // [T][H]
 };
+
+// ---- profiling: events the next kernel launch records around itself ------
+// Set by the forward's timing wrapper; the launch puts them into its own
+// dispatch (start and end timestamps of the kernel itself) and clears them.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+template <typename K, typename... A>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+    if (g_launch_events.start) {
+        const LaunchEvents ev = g_launch_events;
+        g_launch_events = LaunchEvents{};
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    }
+}
 
 // ---- launchers (kernel files) -------------------------------------------
 hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,

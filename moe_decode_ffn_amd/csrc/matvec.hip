@@ -546,9 +546,9 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
     const size_t lds = gate_up_lds_bytes(p, wkind == W_F32 ? 4 : 2);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
 #define GU_LAUNCH(L, N)                                                                          \
-    if (wkind == W_F32) hipLaunchKernelGGL((k_gate_up<W_F32, L, N>), dim3(grid), dim3(256), lds, s, p); \
-    else if (wkind == W_BF16) hipLaunchKernelGGL((k_gate_up<W_BF16, L, N>), dim3(grid), dim3(256), lds, s, p); \
-    else hipLaunchKernelGGL((k_gate_up<W_Q4, L, N>), dim3(grid), dim3(256), lds, s, p);
+    if (wkind == W_F32) launch_kernel(k_gate_up<W_F32, L, N>, dim3(grid), dim3(256), lds, s, p); \
+    else if (wkind == W_BF16) launch_kernel(k_gate_up<W_BF16, L, N>, dim3(grid), dim3(256), lds, s, p); \
+    else launch_kernel(k_gate_up<W_Q4, L, N>, dim3(grid), dim3(256), lds, s, p);
     MOE_ROWMAP_CASES(GU_LAUNCH)
 #undef GU_LAUNCH
     return hipGetLastError();
@@ -557,9 +557,9 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
 hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
 #define D_LAUNCH(L, N)                                                                           \
-    if (wkind == W_F32) hipLaunchKernelGGL((k_down<W_F32, L, N>), dim3(grid), dim3(256), 0, s, p); \
-    else if (wkind == W_BF16) hipLaunchKernelGGL((k_down<W_BF16, L, N>), dim3(grid), dim3(256), 0, s, p); \
-    else hipLaunchKernelGGL((k_down<W_Q4, L, N>), dim3(grid), dim3(256), 0, s, p);
+    if (wkind == W_F32) launch_kernel(k_down<W_F32, L, N>, dim3(grid), dim3(256), 0, s, p); \
+    else if (wkind == W_BF16) launch_kernel(k_down<W_BF16, L, N>, dim3(grid), dim3(256), 0, s, p); \
+    else launch_kernel(k_down<W_Q4, L, N>, dim3(grid), dim3(256), 0, s, p);
     MOE_ROWMAP_CASES(D_LAUNCH)
 #undef D_LAUNCH
     return hipGetLastError();
@@ -567,7 +567,7 @@ hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid
 
 hipError_t launch_join(const JoinParams &p, hipStream_t s) {
     const dim3 grid((p.H + 255) / 256, p.T);
-    hipLaunchKernelGGL(k_join, grid, dim3(256), 0, s, p);
+    launch_kernel(k_join, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -120,13 +120,13 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     P->d = d;
     P->wkind = d.weight_dtype;
     P->gemm_ok = gemm_ok && !(d.flags & MOE_FFN_FORCE_MATVEC);
-    // small-batch threshold: at or below it the shared expert is folded into the
-    // routed launches (fewest launches); above it, where the shared expert's own
-    // work is large, it overlaps the routed chain on the plan's second stream
+    // regime threshold: mat-vec kernels up to it, grouped MFMA GEMM above (bf16
+    // storage).  AUTO folds the shared expert into the routed launches in both
+    // regimes: measured faster than the second stream at every batch tried
     P->matvec_max = d.matvec_max_tokens ? d.matvec_max_tokens : kDefaultMatvecMax;
     const uint32_t mode = d.flags & MOE_FFN_SHARED_MASK;
     P->mode_matvec = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_FUSED : mode;
-    P->mode_gemm = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_AUX : mode;
+    P->mode_gemm = mode == MOE_FFN_SHARED_AUTO ? MOE_FFN_SHARED_FUSED : mode;
 
     const int H = d.hidden, E = d.n_experts, k = d.top_k, I = d.inter, Is = d.shared_inter;
     const size_t T = (size_t)d.max_tokens, P_ = T * k;

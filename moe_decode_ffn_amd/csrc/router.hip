@@ -113,7 +113,7 @@ size_t route_kernel_lds_bytes(int T, int k, int E) {
 hipError_t launch_route(const RouterParams &p, hipStream_t s) {
     const size_t lds = route_kernel_lds_bytes(p.T, p.k, p.E);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * route_kernel_waves(p.T)), lds, s, p);
+    launch_kernel(k_route, dim3(1), dim3(64 * route_kernel_waves(p.T)), lds, s, p);
     return hipGetLastError();
 }
 
@@ -129,9 +129,9 @@ static hipError_t launch_router_t(const RouterParams &p, int grid_rows, int grid
     const size_t lds = router_lds_bytes(p);
     const dim3 grid(grid_rows, grid_tiles);
     if (p.x_bf16)
-        hipLaunchKernelGGL((k_router<LPR, NC, true>), grid, dim3(256), lds, s, p);
+        launch_kernel(k_router<LPR, NC, true>, grid, dim3(256), lds, s, p);
     else
-        hipLaunchKernelGGL((k_router<LPR, NC, false>), grid, dim3(256), lds, s, p);
+        launch_kernel(k_router<LPR, NC, false>, grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 

@@ -112,29 +112,35 @@ def _decode_layer(shape, seed):
 
 
 FULL = {
-    "decode_bf16_t1": (synth.DECODE_BF16, 1, 1),
-    "decode_bf16_t8": (synth.DECODE_BF16, 2, 8),
-    # around the largest batch whose routing the gate/up workgroups compute
-    # themselves (more workgroups than fit on the GPU at once from T = 4 on)
-    "decode_bf16_t4": (synth.DECODE_BF16, 2, 4),
-    "decode_bf16_t16": (synth.DECODE_BF16, 2, 16),
-    "decode_bf16_t17": (synth.DECODE_BF16, 2, 17),
-    "decode_q4_t1": (synth.DECODE_Q4, 3, 1),
-    "decode_q4_t4": (synth.DECODE_Q4, 3, 4),
+    # name: (shape, seed, tokens, regime flags); the default regime switches to the
+    # grouped GEMM above 6 tokens for bf16, so the mat-vec kernels are also forced
+    # at batches beyond it; routing runs in the gate/up launch up to 4 tokens, in
+    # its own launch up to 32 and in the router's tail above
+    "decode_bf16_t1": (synth.DECODE_BF16, 1, 1, 0),
+    "decode_bf16_t4": (synth.DECODE_BF16, 2, 4, 0),
+    "decode_bf16_t5": (synth.DECODE_BF16, 2, 5, 0),
+    "decode_bf16_t7": (synth.DECODE_BF16, 2, 7, 0),
+    "decode_bf16_t8": (synth.DECODE_BF16, 2, 8, 0),
+    "decode_bf16_t8_matvec": (synth.DECODE_BF16, 2, 8, ffn.FORCE_MATVEC),
+    "decode_bf16_t16_matvec": (synth.DECODE_BF16, 2, 16, ffn.FORCE_MATVEC),
+    "decode_bf16_t33": (synth.DECODE_BF16, 2, 33, 0),
+    "decode_q4_t1": (synth.DECODE_Q4, 3, 1, 0),
+    "decode_q4_t4": (synth.DECODE_Q4, 3, 4, 0),
+    "decode_q4_t12": (synth.DECODE_Q4, 3, 12, 0),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_decode_layer_full_size(orc, name):
     dev = device()
-    shape, seed, T = FULL[name]
+    shape, seed, T, regime = FULL[name]
     dl, lc = _decode_layer(shape, seed)
     x = synth.make_tokens(shape, T, seed, stream=T)
     ref = orc.forward(oracle_layer(lc), oracle_tokens(x), nthreads=oracle_threads())
     outs = {}
     for m in MODES:
         print(f"[full] {name} mode={m}", flush=True)
-        mf = _plan(shape, T, m)
+        mf = _plan(shape, T, m, regime)
         got = run_gpu(mf, dl, x.to(dev))
         rep = compare(orc, lc, x, got, tol_for(shape), ref=ref)
         print(f"  {rep}", flush=True)
