@@ -105,6 +105,10 @@ typedef enum moe_ffn_dtype {
  * wrong stream.  They change timing only, never results. */
 #define MOE_FFN_DEBUG_DELAY_AUX 0x100u
 #define MOE_FFN_DEBUG_DELAY_MAIN 0x200u
+/* Test hook: in the mat-vec regime run the down step and the join as two
+ * launches where one (MOE_FFN_K_DOWN_JOIN) would apply.  Results are
+ * bit-identical either way. */
+#define MOE_FFN_DEBUG_SPLIT_JOIN 0x400u
 
 /* Shapes and storage; frozen for the life of the plan.
  * Limits (else MOE_FFN_ERR_UNSUPPORTED): hidden, inter, shared_inter
@@ -179,10 +183,11 @@ typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
     MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */
     MOE_FFN_K_SH_DOWN = 5,      /* down of the shared expert alone (either regime) */
-    MOE_FFN_K_JOIN = 6,         /* weighted sum over slots + sigmoid-gated shared output */
+    MOE_FFN_K_JOIN = 6,         /* weighted sum over slots + sigmoid-gated shared output (GEMM regime) */
     MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up (routed, or routed + shared when fused) */
     MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down (routed, or routed + shared when fused) */
-    MOE_FFN_K_COUNT = 9
+    MOE_FFN_K_DOWN_JOIN = 9,    /* mat-vec regime: down of every pair of a row tile + the join */
+    MOE_FFN_K_COUNT = 10
 } moe_ffn_kernel_id;
 
 int32_t moe_ffn_abi_version(void);

@@ -7,7 +7,8 @@
 //           to 32 tokens) or in the router launch's tail (above)
 //   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
 //   down    y = down h per pair [+ S for the shared expert]
-//   join    out = sum_j w_j y_j + s * S
+//   join    out = sum_j w_j y_j + s * S (mat-vec regime: k_down_join does the
+//           down step and the join in one launch)
 // gate/up and down are mat-vec kernels (matvec.hip) up to matvec_max tokens and
 // grouped MFMA GEMMs (gemm.hip) above it when the storage is bf16.
 // Where the shared expert's gate/up and down run (page "ggml-cuda: overlap the
@@ -281,6 +282,16 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     const int gg_tb = (Ti + 16 * gg_nt - 1) / (16 * gg_nt);
     auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
 
+    // mat-vec regime: down and join in one launch when the row tile's y fits in LDS
+    const bool use_dj = !gemm && !(d.flags & MOE_FFN_DEBUG_SPLIT_JOIN) &&
+                        down_join_lds_bytes(Ti, (int)k, P->map_down) <= kLdsLimit;
+    DownJoinParams djp{};
+    djp.T = Ti; djp.H = (int)H; djp.k = (int)k; djp.E = (int)E;
+    djp.wd = (const uint8_t *)t->w_down; djp.sd = t->w_down_scale; djp.I = (int)I; djp.h = h;
+    djp.pairs = pairs; djp.pos_expert = pos_expert;
+    djp.swd = (const uint8_t *)t->sh_down; djp.ssd = t->sh_down_scale; djp.Is = (int)Is; djp.hs = sh_h;
+    djp.S = sh_S; djp.wts = wts; djp.gate_s = gate_s; djp.out = t->out;
+
     JoinParams jp{};
     jp.T = Ti; jp.H = (int)H; jp.k = (int)k; jp.y = y; jp.wts = wts; jp.gate_s = gate_s;
     jp.S = sh_S; jp.out = t->out;
@@ -359,6 +370,17 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     auto chk = [&](hipError_t x) {
         if (err == hipSuccess && x != hipSuccess) err = x;
     };
+    // the routed down step and the join: one launch (k_down_join) or two
+    auto run_tail = [&](hipStream_t s, bool shared_here) {
+        if (!use_dj) {
+            hipError_t e1 = step_down(s, true, shared_here);
+            if (e1 != hipSuccess) return e1;
+            return run_join(s);
+        }
+        DownJoinParams q = djp;
+        q.shared_here = shared_here ? 1 : 0;
+        return timed(P, MOE_FFN_K_DOWN_JOIN, s, [&] { return launch_down_join(q, wk, P->map_down, s); });
+    };
     if (mode == MOE_FFN_SHARED_AUX) {
         chk(hipEventRecord(P->ev_fork, stream));
         chk(hipStreamWaitEvent(P->aux, P->ev_fork, 0));
@@ -369,9 +391,14 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(step_gate_up(stream, true, false));
-        chk(step_down(stream, true, false));
-        chk(hipStreamWaitEvent(stream, P->ev_join, 0));
-        chk(run_join(stream));
+        if (use_dj) {  // the fused launch reads S: wait for the shared branch first
+            chk(hipStreamWaitEvent(stream, P->ev_join, 0));
+            chk(run_tail(stream, false));
+        } else {
+            chk(step_down(stream, true, false));
+            chk(hipStreamWaitEvent(stream, P->ev_join, 0));
+            chk(run_join(stream));
+        }
     } else if (mode == MOE_FFN_SHARED_SEQ) {
         if (delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(step_gate_up(stream, false, true));
@@ -379,14 +406,12 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         if (delay_main) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(step_gate_up(stream, true, false));
-        chk(step_down(stream, true, false));
-        chk(run_join(stream));
+        chk(run_tail(stream, false));
     } else {  // FUSED
         if (delay_main || delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(run_router(stream));
         chk(step_gate_up(stream, true, true));
-        chk(step_down(stream, true, true));
-        chk(run_join(stream));
+        chk(run_tail(stream, true));
     }
     if (err != hipSuccess) return hip_fail(err, "kernel launch");
     if ((err = hipGetLastError()) != hipSuccess) return hip_fail(err, "kernel launch");

@@ -178,6 +178,25 @@ struct DownParams {
     int tiles_shared;
 };
 
+struct DownJoinParams {
+    int T, H, k, E;
+    const uint8_t *wd;      // [E][H] rows of I
+    const uint16_t *sd;     // [E][H][I/32]
+    int I;
+    const float *h;         // [T*k][I]
+    const int *pairs;       // [T*k] bucketed order
+    const int *pos_expert;  // [T*k]
+    const uint8_t *swd;     // [H] rows of Is
+    const uint16_t *ssd;
+    int Is;
+    const float *hs;        // [T][Is]
+    int shared_here;        // 1: the shared expert's down runs here; 0: S comes from memory
+    const float *S;         // [T][H] (shared_here == 0)
+    const float *wts;       // [T*k]
+    const float *gate_s;    // [T]
+    float *out;             // [T][H]
+};
+
 struct GGParams {
     const void *x;       // [T][H] bf16
     int T, H, k, E, I, Is;
@@ -227,6 +246,9 @@ hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, 
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_join(const JoinParams &p, hipStream_t s);
+hipError_t launch_down_join(const DownJoinParams &p, int wkind, const RowMap &m, hipStream_t s);
+int down_join_rows_per_wg(const RowMap &m);
+size_t down_join_lds_bytes(int T, int k, const RowMap &m);
 hipError_t launch_gg_gate_up(const GGParams &p, int nt, int grid, hipStream_t s);
 hipError_t launch_gg_down(const GGParams &p, int nt, int grid, hipStream_t s);
 int gg_occupancy(bool gate_up, int nt);

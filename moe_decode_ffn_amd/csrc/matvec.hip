@@ -15,8 +15,12 @@
 //   one expert per job.
 // k_join:    out = sum_j w_j y_j (slot order) + s * S, product and sum rounded
 //   separately.
+// k_down_join: down + join in one launch for small batches: a workgroup of 16
+//   waves owns a tile of output rows for every pair, keeps y in LDS and joins.
 // Storage: fp32, bf16, or 4-bit blocks (32 elements + one fp16 scale per block,
 // dequantised in registers).
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 #include "routing.h"
@@ -493,6 +497,117 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
     }
 }
 
+// ---- down + join: one workgroup per tile of output rows (small batches) ---------------------
+constexpr int kDJWaves = 16;
+
+// Rows per lane segment of a unit: 8 rows per tile when a row takes one chunk
+// per lane, fewer when it takes several.
+template <int LPR, int NC>
+constexpr int dj_rpw() {
+    return (8 * LPR / 64) / NC > 1 ? (8 * LPR / 64) / NC : 1;
+}
+
+// A unit is one (token, slot) pair in bucketed order, or one token of the
+// shared expert, over the workgroup's whole row tile; 16 waves take units in
+// turn, so at small batches every unit's loads are in flight at once.  y for
+// the tile stays in LDS and the join runs in place, with the same dot
+// products (down_dot + seg_sum over the same row map) and the same join
+// arithmetic as k_down + k_join: the results are bit-identical to them.
+template <int WK, int LPR, int NC>
+__global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
+    constexpr int RPW = dj_rpw<LPR, NC>();
+    constexpr int RPI = 64 / LPR;
+    constexpr int RT = RPW * RPI;  // rows of the tile
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / LPR, sl = lane % LPR;
+    const int H = p.H, T = p.T, k = p.k, E = p.E;
+    const int NP = T * k, NU = NP + (p.shared_here ? T : 0);
+    const int r0 = blockIdx.x * RT;
+    int *s_pairs = reinterpret_cast<int *>(lds);          // [NP]
+    int *s_pose = s_pairs + NP;                           // [NP]
+    float *s_w = reinterpret_cast<float *>(s_pose + NP);  // [NP]
+    float *s_g = s_w + NP;                                // [T]
+    float *s_y = s_g + T;                                 // [NP + T][RT]
+    for (int i = tid; i < NP; i += blockDim.x) {
+        s_pairs[i] = p.pairs[i];
+        s_pose[i] = p.pos_expert[i];
+        s_w[i] = p.wts[i];
+    }
+    for (int i = tid; i < T; i += blockDim.x) s_g[i] = p.gate_s[i];
+    __syncthreads();
+
+    for (int u = wave; u < NU; u += kDJWaves) {
+        const uint8_t *W;
+        const uint16_t *Sc = nullptr;
+        const float *act;
+        int K, slot;
+        bool ok = true;
+        if (u < NP) {
+            const int e = s_pose[u], pr = s_pairs[u];
+            ok = e >= 0 && e < E && pr >= 0 && pr < NP;
+            const size_t m0 = (size_t)(ok ? e : 0) * H;
+            W = p.wd + m0 * row_bytes<WK>(p.I);
+            if constexpr (WK == W_Q4) Sc = p.sd + m0 * (p.I / 32);
+            act = p.h + (size_t)(ok ? pr : 0) * p.I;
+            K = p.I;
+            slot = ok ? pr : 0;
+        } else {
+            const int t = u - NP;
+            W = p.swd;
+            if constexpr (WK == W_Q4) Sc = p.ssd;
+            act = p.hs + (size_t)t * p.Is;
+            K = p.Is;
+            slot = NP + t;
+        }
+        const size_t rb = row_bytes<WK>(K);
+        const int nch = (int)(rb / 16), nsb = K / 32;
+        uint4 w[RPW][NC];
+        float sc[RPW][NC];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = r0 + i * RPI + seg;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const int c = sl + LPR * n;
+                const bool v = ok && r < H && c < nch;
+                w[i][n] = v ? ld16(W + (size_t)r * rb + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
+                if constexpr (WK == W_Q4) sc[i][n] = v ? f16_to_f32(Sc[(size_t)r * nsb + c]) : 0.f;
+            }
+        }
+        ActChunks<WK, NC> ac;
+        load_act<WK, LPR, NC>(act, ok ? nch : 0, sl, ac);
+        float asum[NC];
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            asum[n] = 0.f;
+            if constexpr (WK == W_Q4) {
+#pragma unroll
+                for (int q = 0; q < 32; q += 4)
+                    asum[n] += (ac.v[n][q] + ac.v[n][q + 1]) + (ac.v[n][q + 2] + ac.v[n][q + 3]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const float v = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(ac, asum, nch, sl, w, sc, i));
+            if (sl == 0 && ok) s_y[slot * RT + i * RPI + seg] = v;
+        }
+    }
+    __syncthreads();
+
+    // join for the tile's rows of every token (k_join's arithmetic)
+    for (int i = tid; i < T * RT; i += blockDim.x) {
+        const int t = i / RT, rr = i - t * RT, r = r0 + rr;
+        if (r >= H) continue;
+        const float *yt = s_y + (size_t)t * k * RT + rr;
+        const float *wt = s_w + (size_t)t * k;
+        float routed = wt[0] * yt[0];
+        for (int j = 1; j < k; ++j) routed = fmaf(wt[j], yt[(size_t)j * RT], routed);
+        const float S = p.shared_here ? s_y[(size_t)(NP + t) * RT + rr] : p.S[(size_t)t * H + r];
+        p.out[(size_t)t * H + r] = __fadd_rn(routed, __fmul_rn(s_g[t], S));
+    }
+}
+
 // ---- join ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_join(JoinParams p) {
     const int t = blockIdx.y;
@@ -562,6 +677,30 @@ hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid
     else launch_kernel(k_down<W_Q4, L, N>, dim3(grid), dim3(256), 0, s, p);
     MOE_ROWMAP_CASES(D_LAUNCH)
 #undef D_LAUNCH
+    return hipGetLastError();
+}
+
+int down_join_rows_per_wg(const RowMap &m) {
+    const int rpw = std::max(1, (8 * m.lpr / 64) / m.nc);
+    return rpw * (64 / m.lpr);
+}
+
+size_t down_join_lds_bytes(int T, int k, const RowMap &m) {
+    const size_t np = (size_t)T * k;
+    return (3 * np + T) * 4 + (np + T) * (size_t)down_join_rows_per_wg(m) * 4;
+}
+
+hipError_t launch_down_join(const DownJoinParams &p, int wkind, const RowMap &m, hipStream_t s) {
+    const size_t lds = down_join_lds_bytes(p.T, p.k, m);
+    if (lds > kLdsLimit) return hipErrorInvalidValue;
+    const int rows = down_join_rows_per_wg(m);
+    const int grid = (p.H + rows - 1) / rows;
+#define DJ_LAUNCH(L, N)                                                                                    \
+    if (wkind == W_F32) launch_kernel(k_down_join<W_F32, L, N>, dim3(grid), dim3(64 * kDJWaves), lds, s, p); \
+    else if (wkind == W_BF16) launch_kernel(k_down_join<W_BF16, L, N>, dim3(grid), dim3(64 * kDJWaves), lds, s, p); \
+    else launch_kernel(k_down_join<W_Q4, L, N>, dim3(grid), dim3(64 * kDJWaves), lds, s, p);
+    MOE_ROWMAP_CASES(DJ_LAUNCH)
+#undef DJ_LAUNCH
     return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     if (!desc || !out_plan) return set_error(MOE_FFN_ERR_INVALID_ARG, "desc and out_plan must not be NULL");
     const moe_ffn_desc d = *desc;
     const uint32_t known = MOE_FFN_SHARED_MASK | MOE_FFN_FORCE_MATVEC | MOE_FFN_FORCE_GEMM |
-                           MOE_FFN_DEBUG_DELAY_AUX | MOE_FFN_DEBUG_DELAY_MAIN;
+                           MOE_FFN_DEBUG_DELAY_AUX | MOE_FFN_DEBUG_DELAY_MAIN | MOE_FFN_DEBUG_SPLIT_JOIN;
     if (d.flags & ~known) return set_error(MOE_FFN_ERR_INVALID_ARG, "unknown flag bits");
     if ((d.flags & MOE_FFN_FORCE_MATVEC) && (d.flags & MOE_FFN_FORCE_GEMM))
         return set_error(MOE_FFN_ERR_INVALID_ARG, "FORCE_MATVEC and FORCE_GEMM are exclusive");

@@ -20,6 +20,34 @@
 namespace moeffn {
 
 constexpr int kRouterWaves = 4;
+constexpr int kRouterTile = 8;  // most tokens per workgroup column
+
+// Sums eight values across each aligned segment of LPR lanes (LPR in 8..64) in
+// one transposed butterfly: three halving exchanges leave every lane holding a
+// partial sum of one token (tok = the lane's bits LPR/2, LPR/4, LPR/8), and the
+// LPR/8 lanes that share a token finish the sum; all of them hold identical bits.
+template <int LPR>
+__device__ __forceinline__ float seg_sum8(const float (&a)[8], int sl, int &tok) {
+    constexpr int d1 = LPR / 2, d2 = LPR / 4, d3 = LPR / 8;
+    const bool h1 = (sl & d1) != 0, h2 = (sl & d2) != 0, h3 = (sl & d3) != 0;
+    float b[4], c[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = h1 ? a[i] : a[i + 4], keep = h1 ? a[i + 4] : a[i];
+        b[i] = keep + __shfl_xor(send, d1);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = h2 ? b[i] : b[i + 2], keep = h2 ? b[i + 2] : b[i];
+        c[i] = keep + __shfl_xor(send, d2);
+    }
+    const float send = h3 ? c[0] : c[1], keep = h3 ? c[1] : c[0];
+    float v = keep + __shfl_xor(send, d3);
+#pragma unroll
+    for (int m = d3 / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    tok = (h1 ? 4 : 0) + (h2 ? 2 : 0) + (h3 ? 1 : 0);
+    return v;
+}
 
 int router_rows_per_wg(const RowMap &m) { return kRouterWaves * (64 / m.lpr); }
 
@@ -51,28 +79,35 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         reinterpret_cast<uint4 *>(lds)[i] = ld16(xs + 16 * (size_t)i);
     __syncthreads();
 
-    for (int i = 0; i < nt; ++i) {
-        float acc = 0.f;
+    // partial dot products of up to 8 tokens, then one transposed reduction for all
+    float acc[kRouterTile];
 #pragma unroll
-        for (int n = 0; n < NC; ++n) {
-            const int c = sl + LPR * n;
-            if (c < n_chunks) {
-                float4 xv;
-                if constexpr (XBF) {
-                    const uint2 b = *reinterpret_cast<const uint2 *>(lds + i * xrow + 8 * c);
-                    xv = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
-                } else {
-                    xv = *reinterpret_cast<const float4 *>(lds + i * xrow + 16 * c);
+    for (int i = 0; i < kRouterTile; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = sl + LPR * n;
+        if (c < n_chunks) {
+#pragma unroll
+            for (int i = 0; i < kRouterTile; ++i) {
+                if (i < nt) {
+                    float4 xv;
+                    if constexpr (XBF) {
+                        const uint2 b = *reinterpret_cast<const uint2 *>(lds + i * xrow + 8 * c);
+                        xv = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+                    } else {
+                        xv = *reinterpret_cast<const float4 *>(lds + i * xrow + 16 * c);
+                    }
+                    acc[i] = fmaf(w[n].x, xv.x, acc[i]);
+                    acc[i] = fmaf(w[n].y, xv.y, acc[i]);
+                    acc[i] = fmaf(w[n].z, xv.z, acc[i]);
+                    acc[i] = fmaf(w[n].w, xv.w, acc[i]);
                 }
-                acc = fmaf(w[n].x, xv.x, acc);
-                acc = fmaf(w[n].y, xv.y, acc);
-                acc = fmaf(w[n].z, xv.z, acc);
-                acc = fmaf(w[n].w, xv.w, acc);
             }
         }
-        acc = seg_sum<LPR>(acc);
-        if (valid && sl == 0) p.logits[(size_t)(t0 + i) * (E + 1) + row] = acc;
     }
+    int tok = 0;
+    const float sum = seg_sum8<LPR>(acc, sl, tok);
+    if (valid && (sl & (LPR / 8 - 1)) == 0 && tok < nt) p.logits[(size_t)(t0 + tok) * (E + 1) + row] = sum;
 
     // ---- routing tail ----
     if (!p.route_tail) return;

@@ -24,10 +24,10 @@ F32, BF16, Q4_B32 = 0, 1, 2
 # flags
 SHARED_AUTO, SHARED_AUX, SHARED_SEQ, SHARED_FUSED, SHARED_MASK = 0x0, 0x1, 0x2, 0x3, 0x3
 FORCE_MATVEC, FORCE_GEMM = 0x10, 0x20
-DEBUG_DELAY_AUX, DEBUG_DELAY_MAIN = 0x100, 0x200
+DEBUG_DELAY_AUX, DEBUG_DELAY_MAIN, DEBUG_SPLIT_JOIN = 0x100, 0x200, 0x400
 # moe_ffn_kernel_id
 KERNELS = ("router", "route", "gate_up", "down", "sh_gate_up", "sh_down", "join", "gg_gate_up",
-           "gg_down")
+           "gg_down", "down_join")
 K_COUNT = len(KERNELS)
 
 DTYPES = {"f32": F32, "bf16": BF16, "q4": Q4_B32}

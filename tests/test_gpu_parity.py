@@ -177,6 +177,30 @@ def test_decode_bf16_t128(orc):
     mf.close()
 
 
+SPLIT_JOIN_CASES = {
+    # name: (shape, seed, tokens): the one-launch down + join against separate launches
+    "tiny_fp32": (synth.TINY, 0, 3),
+    "bf16_ragged_chunks": (synth.LayerShape(160, 12, 3, 96, 64, "bf16", "bf16"), 5, 6),
+    "q4_wide": (synth.LayerShape(1024, 16, 4, 256, 128, "bf16", "q4"), 11, 6),
+    "bf16_wide_rows": (synth.LayerShape(512, 16, 4, 2048, 1024, "bf16", "bf16"), 24, 5),
+    "decode_bf16_t1": (synth.DECODE_BF16, 1, 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_JOIN_CASES))
+def test_down_join_fused_matches_split(name):
+    """One launch for down + join gives the same bits as two, in every shared mode."""
+    dev = device()
+    shape, seed, T = SPLIT_JOIN_CASES[name]
+    dl = synth.layer_to(synth.make_layer(shape, seed), dev)
+    x = synth.make_tokens(shape, T, seed, stream=T).to(dev)
+    for m in MODES:
+        print(f"[split-join] {name} T={T} mode={m}", flush=True)
+        fused = run_gpu(_plan(shape, T, m, ffn.FORCE_MATVEC), dl, x)["out"]
+        split = run_gpu(_plan(shape, T, m, ffn.FORCE_MATVEC | ffn.DEBUG_SPLIT_JOIN), dl, x)["out"]
+        assert torch.equal(fused, split), f"mode {m}"
+
+
 def test_many_pairs_top16(orc):
     """256 tokens x top-16 over 64 experts: 4096 pairs, big buckets."""
     dev = device()
