@@ -20,7 +20,13 @@
  * gate/up inputs).  The pages print no formula for routing or for the shared
  * gate; the plain reading taken here is the usual one for this layer type:
  *
- *   for each token x:
+ *   for each token x0 (the layer's input):
+ *     0. input norm  (optional) x[h] = (x0[h] * rho) * wn[h],
+ *                    rho = 1 / sqrt(sum_h x0[h]^2 / H + eps); else x = x0.
+ *                    The FFN-input RMSNorm is the fork point of both branches
+ *                    (same page, commit messages), RMSNorm followed by a
+ *                    multiply with a one-dimensional weight (page "ggml operator
+ *                    extensions", section "sd.cpp integration").
  *     1. logits      l[e] = sum_h x[h] * Wr[e][h]                  e < E
  *     2. selection   experts ranked by (l descending, index ascending);
  *                    ids = the first k, in rank order (exact ties -> lower index)
@@ -32,6 +38,9 @@
  *     7. shared      S = Ws_d . (silu(Ws_g . x) * (Ws_u . x)),
  *                    s = 1 / (1 + exp(-(wg . x)))
  *     8. output      out = r + s * S
+ *     9. residual    (optional) out = x0 + (r + s * S), the block's residual add
+ *                    after the join (same page and section: gate multiply, then
+ *                    residual add)
  *
  * 4-bit block storage (the pages do not give one): a block is 32 consecutive
  * elements along a row's reduction dimension; element c of a row sits in byte
@@ -62,6 +71,9 @@ typedef struct {
     orc_matrix sh_gate, sh_up;  /* rows = I_s, cols = H                          */
     orc_matrix sh_down;         /* rows = H, cols = I_s                          */
     const float *gate_vec;      /* [H]                                           */
+    const float *norm_w;        /* [H] RMSNorm weight, or NULL: no input norm     */
+    double norm_eps;            /* RMSNorm epsilon (with norm_w)                  */
+    int residual;               /* 1: out = x0 + layer output                     */
 } orc_layer;
 
 /* ---- exact decoders ---------------------------------------------------- */
@@ -170,6 +182,8 @@ int orc_forward(const orc_layer *L, long n_tokens, int nthreads, const int32_t *
     const long Is = L->shared_inter;
     if (H <= 0 || E <= 0 || K <= 0 || K > E || I <= 0 || Is <= 0 || n_tokens < 0 || !out)
         return -1;
+    if (L->norm_w && !(L->norm_eps >= 0.0))
+        return -1;
     if (nthreads < 1)
         nthreads = 1;
     if (forced_ids)
@@ -177,6 +191,7 @@ int orc_forward(const orc_layer *L, long n_tokens, int nthreads, const int32_t *
             if (forced_ids[i] < 0 || forced_ids[i] >= E)
                 return -1;
 
+    double *x0 = malloc(sizeof(double) * H);
     double *x = malloc(sizeof(double) * H);
     double *l = malloc(sizeof(double) * E);
     double *p = malloc(sizeof(double) * E);
@@ -189,7 +204,19 @@ int orc_forward(const orc_layer *L, long n_tokens, int nthreads, const int32_t *
 
     for (long t = 0; t < n_tokens; ++t) {
         for (long h = 0; h < H; ++h)
-            x[h] = token_elem(L, t, h);
+            x0[h] = token_elem(L, t, h);
+
+        /* 0. optional RMSNorm of the input */
+        if (L->norm_w) {
+            double ss = 0.0;
+            for (long h = 0; h < H; ++h)
+                ss += x0[h] * x0[h];
+            double rho = 1.0 / sqrt(ss / (double)H + L->norm_eps);
+            for (long h = 0; h < H; ++h)
+                x[h] = (x0[h] * rho) * (double)L->norm_w[h];
+        } else {
+            memcpy(x, x0, sizeof(double) * H);
+        }
 
         /* 1. router logits */
         for (long e = 0; e < E; ++e) {
@@ -251,9 +278,11 @@ int orc_forward(const orc_layer *L, long n_tokens, int nthreads, const int32_t *
             gl += (double)L->gate_vec[h] * x[h];
         double s = sigmoid(gl);
 
-        /* 8. join */
-        for (long h = 0; h < H; ++h)
-            out[t * H + h] = r[h] + s * S[h];
+        /* 8. join, 9. optional residual */
+        for (long h = 0; h < H; ++h) {
+            const double joined = r[h] + s * S[h];
+            out[t * H + h] = L->residual ? x0[h] + joined : joined;
+        }
 
         if (routed)
             memcpy(routed + t * H, r, sizeof(double) * H);
@@ -270,6 +299,7 @@ int orc_forward(const orc_layer *L, long n_tokens, int nthreads, const int32_t *
             gate_s[t] = s;
     }
 
+    free(x0);
     free(x);
     free(l);
     free(p);

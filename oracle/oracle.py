@@ -11,7 +11,8 @@ Two independent implementations of the same definition live here:
 * ``brute_force`` is a numpy fp64 twin written separately: it evaluates *every*
   expert on every token, then selects and combines.  Agreement of the two on
   small layers checks selection, renormalisation and the final identity
-  out = sum_j w_j E_{ids_j}(x) + sigmoid(wg . x) S(x).
+  out = sum_j w_j E_{ids_j}(x) + sigmoid(wg . x) S(x), with the optional input
+  RMSNorm (x = RMSNorm(x0) * wn) and residual (out += x0) around it.
 
 The layer definition, its citations and the 4-bit storage reading are in the C
 file's header comment.  Inputs are plain numpy arrays:
@@ -22,6 +23,7 @@ file's header comment.  Inputs are plain numpy arrays:
   down      ...                      [E,H,I]       or uint8 [E,H,I/2]
   sh_gate, sh_up [I_s,H]; sh_down [H,I_s] (same storage as the experts)
   *_scale   uint16 fp16 bits [..., K/32] for 4-bit storage, else None
+  norm_w    float32 [H] or None (input RMSNorm weight; norm_eps its epsilon)
 """
 from __future__ import annotations
 
@@ -59,7 +61,8 @@ class _Layer(ctypes.Structure):
                 ("x", ctypes.c_void_p), ("router", ctypes.c_void_p),
                 ("gate", _Matrix), ("up", _Matrix), ("down", _Matrix),
                 ("sh_gate", _Matrix), ("sh_up", _Matrix), ("sh_down", _Matrix),
-                ("gate_vec", ctypes.c_void_p)]
+                ("gate_vec", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_double), ("residual", ctypes.c_int)]
 
 
 class Oracle:
@@ -157,15 +160,19 @@ class OracleLayer:
     sh_gate_scale: np.ndarray | None = None
     sh_up_scale: np.ndarray | None = None
     sh_down_scale: np.ndarray | None = None
+    norm_w: np.ndarray | None = None      # float32 [H]: RMSNorm of the input first
+    norm_eps: float = 0.0
+    residual: bool = False                # out = x + layer output
 
     def __post_init__(self):
         for name in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down", "gate_vec",
                      "gate_scale", "up_scale", "down_scale", "sh_gate_scale", "sh_up_scale",
-                     "sh_down_scale"):
+                     "sh_down_scale", "norm_w"):
             v = getattr(self, name)
             if v is not None:
                 setattr(self, name, np.ascontiguousarray(v))
         assert self.router.dtype == np.float32 and self.gate_vec.dtype == np.float32
+        assert self.norm_w is None or self.norm_w.dtype == np.float32
 
     def ctypes_layer(self, x: np.ndarray) -> _Layer:
         H, E, I, Is = self.hidden, self.n_experts, self.inter, self.shared_inter
@@ -185,6 +192,9 @@ class OracleLayer:
         L.sh_up = _matrix(self.sh_up, self.sh_up_scale, k, Is, H)
         L.sh_down = _matrix(self.sh_down, self.sh_down_scale, k, H, Is)
         L.gate_vec = self.gate_vec.ctypes.data
+        L.norm_w = None if self.norm_w is None else self.norm_w.ctypes.data
+        L.norm_eps = float(self.norm_eps)
+        L.residual = 1 if self.residual else 0
         self._keepalive = (x,)
         return L
 
@@ -236,7 +246,12 @@ def np_decode(w: np.ndarray, scale: np.ndarray | None, kind: str) -> np.ndarray:
 def brute_force(layer: OracleLayer, x: np.ndarray) -> dict:
     """Evaluate all E experts on every token, then select, weight and join."""
     k = layer.w_kind
-    X = x.astype(np.float64) if layer.x_kind == "f32" else np_bf16(x)        # [T,H]
+    X0 = x.astype(np.float64) if layer.x_kind == "f32" else np_bf16(x)       # [T,H]
+    if layer.norm_w is not None:                                              # RMSNorm, then weight
+        rho = 1.0 / np.sqrt(np.mean(X0 * X0, axis=1, keepdims=True) + layer.norm_eps)
+        X = X0 * rho * layer.norm_w.astype(np.float64)
+    else:
+        X = X0
     Wg = np_decode(layer.gate, layer.gate_scale, k)                           # [E,I,H]
     Wu = np_decode(layer.up, layer.up_scale, k)
     Wd = np_decode(layer.down, layer.down_scale, k)                           # [E,H,I]
@@ -258,5 +273,7 @@ def brute_force(layer: OracleLayer, x: np.ndarray) -> dict:
     S = (Sg / (1.0 + np.exp(-Sg)) * Su) @ np_decode(layer.sh_down, layer.sh_down_scale, k).T
     s = 1.0 / (1.0 + np.exp(-(X @ layer.gate_vec.astype(np.float64))))
     out = routed + s[:, None] * S
+    if layer.residual:
+        out = X0 + out
     return {"out": out, "routed": routed, "shared": S, "gate": s, "ids": ids.astype(np.int32),
             "weights": w, "logits": logits, "all_experts": Y}

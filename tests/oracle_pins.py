@@ -321,6 +321,65 @@ def pin_forced_ids(orc):
         _close(f["out"][t], mix + b["gate"][t] * b["shared"][t], what="forced ids")
 
 
+# ------------------------------------------------- input norm and residual
+
+def _with_block(L: OracleLayer, seed: int, eps: float, residual: bool = True) -> OracleLayer:
+    w = np.random.default_rng(seed).uniform(0.5, 1.5, L.hidden).astype(np.float32)
+    return dataclasses.replace(L, norm_w=w, norm_eps=eps, residual=residual)
+
+
+def pin_block_matches_torch_rms_norm(orc):
+    # E = k = 1: out = x0 + SwiGLU(rms_norm(x0) * w) + s(.) * S(.), all from torch routines; the
+    # tokens are scaled down so that eps is not negligible against their mean square
+    for shape, seed, scale in ((synth.LayerShape(64, 1, 1, 48, 32, "f32", "f32"), 151, 0.05),
+                               (synth.LayerShape(96, 1, 1, 64, 32, "f32", "q4"), 152, 1.0)):
+        L0, x = _layer(shape, seed)
+        x = (x * np.float32(scale)).astype(np.float32)
+        L = _with_block(L0, seed, eps=1e-3)
+        r = orc.forward(L, x)
+        X0 = _x64(L, x)
+        X = F.rms_norm(X0, (L.hidden,), weight=torch.from_numpy(L.norm_w.astype(np.float64)),
+                       eps=L.norm_eps)
+        routed = _torch_ffn(X, _w64(L, "gate")[0], _w64(L, "up")[0], _w64(L, "down")[0])
+        S = _torch_ffn(X, _w64(L, "sh_gate"), _w64(L, "sh_up"), _w64(L, "sh_down"))
+        s = torch.sigmoid(X @ torch.from_numpy(L.gate_vec.astype(np.float64)))
+        _close(r["logits"], (X @ torch.from_numpy(L.router.astype(np.float64)).T).numpy(),
+               what="logits of the normalised input")
+        _close(r["out"], (X0 + (routed + s[:, None] * S)).numpy(), what="norm + layer + residual")
+        plain = orc.forward(dataclasses.replace(L, residual=False), x)
+        _close(plain["out"], (routed + s[:, None] * S).numpy(), what="norm without residual")
+
+
+def pin_norm_scale_invariance(orc):
+    # eps = 0: RMSNorm removes any positive scale of the input exactly (up to fp64 rounding)
+    L0, x = _layer(SMALL, 161)
+    L = _with_block(L0, 161, eps=0.0, residual=False)
+    a = orc.forward(L, x)
+    b = orc.forward(L, (x * np.float32(4.0)).astype(np.float32))
+    _close(b["out"], a["out"], rtol=1e-12, what="norm(4 x) = norm(x)")
+    assert np.array_equal(a["ids"], b["ids"]), "scaled input must route the same"
+
+
+def pin_residual_around_a_zero_layer(orc):
+    # every FFN weight zero: the layer output is 0 and the block returns its input exactly
+    L0, x = _layer(SMALL_BF16, 171)
+    L = _with_block(L0, 171, eps=1e-6)
+    for name in ("down", "sh_down"):
+        setattr(L, name, np.zeros_like(getattr(L, name)))
+    r = orc.forward(L, x)
+    assert np.array_equal(r["out"], _x64(L, x).numpy()), "zero layer: out = x0"
+
+
+def pin_brute_force_twin_with_block(orc):
+    for shape, seed, T in ((SMALL, 181, 3), (SMALL_BF16, 182, 2), (SMALL_Q4, 183, 2)):
+        L0, x = _layer(shape, seed, T)
+        L = _with_block(L0, seed, eps=1e-5)
+        r = orc.forward(L, x)
+        b = brute_force(L, x)
+        assert np.array_equal(r["ids"], b["ids"]), "ids with input norm"
+        _close(r["out"], b["out"], rtol=1e-11, what="C oracle vs numpy twin, norm + residual")
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}
 
 

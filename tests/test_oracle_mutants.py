@@ -24,8 +24,15 @@ MUTANTS = {
     "sigmoid_sign": ("1.0 / (1.0 + exp(-z))", "1.0 / (1.0 + exp(z))"),
     "gate_up_swapped": ("a[i] = silu(g[i]) * u[i];", "a[i] = silu(u[i]) * g[i];"),
     "up_matrix_for_gate": ("matvec(G, g0, n_inter, x, g, nthreads)", "matvec(U, g0, n_inter, x, g, nthreads)"),
-    "shared_term_dropped": ("out[t * H + h] = r[h] + s * S[h]", "out[t * H + h] = r[h]"),
-    "shared_gate_dropped": ("out[t * H + h] = r[h] + s * S[h]", "out[t * H + h] = r[h] + S[h]"),
+    "shared_term_dropped": ("const double joined = r[h] + s * S[h];", "const double joined = r[h];"),
+    "shared_gate_dropped": ("const double joined = r[h] + s * S[h];", "const double joined = r[h] + S[h];"),
+    "residual_of_normed_input": ("x0[h] + joined", "x[h] + joined"),
+    "residual_ignored": ("L->residual ? x0[h] + joined : joined", "joined"),
+    "norm_eps_outside_root": ("sqrt(ss / (double)H + L->norm_eps)", "sqrt(ss / (double)H) + L->norm_eps"),
+    "norm_sum_not_mean": ("sqrt(ss / (double)H + L->norm_eps)", "sqrt(ss + L->norm_eps)"),
+    "norm_not_inverted": ("double rho = 1.0 / sqrt(", "double rho = sqrt("),
+    "norm_weight_dropped": ("(x0[h] * rho) * (double)L->norm_w[h]", "(x0[h] * rho)"),
+    "norm_skipped": ("if (L->norm_w) {", "if (0) {"),
     "no_renormalisation": ("wsel[j] = p[sel[j]] / psum", "wsel[j] = p[sel[j]]"),
     "ties_to_higher_index": ("!taken[e] && (best < 0 || l[e] > l[best])", "!taken[e] && (best < 0 || l[e] >= l[best])"),
     "topk_smallest": ("!taken[e] && (best < 0 || l[e] > l[best])", "!taken[e] && (best < 0 || l[e] < l[best])"),
