@@ -54,6 +54,8 @@ def main() -> int:
     ap.add_argument("--regime", default="auto", choices=["auto", "matvec", "gemm"])
     ap.add_argument("--tokens", type=int, default=0, help="override the workload's batch (sweeps)")
     ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--input-block", action="store_true",
+                    help="also run the FFN-input RMSNorm (eps 1e-6) and the residual add")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic", default=None,
@@ -83,9 +85,11 @@ def main() -> int:
     # ---- inputs resident in HBM -----------------------------------------------------
     L = LAYER_COPIES[shape.w_dtype] if shape.hidden >= 1024 else 2
     layers = [synth.make_layer_device(shape, 100 + i, dev) for i in range(L)]
+    if args.input_block:
+        layers = [synth.with_input_block(ly, 500 + i, eps=1e-6) for i, ly in enumerate(layers)]
     xs = [synth.make_tokens_device(shape, T, 1000 + j, dev) for j in range(TOKEN_POOL)]
     regime = {"auto": 0, "matvec": ffn.FORCE_MATVEC, "gemm": ffn.FORCE_GEMM}[args.regime]
-    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=mode | regime)
+    mf = ffn.MoeFfn.for_layer(layers[0], max_tokens=T, flags=mode | regime)
     info = mf.info()
     ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
@@ -178,6 +182,7 @@ def main() -> int:
     rec = read_summary(args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.md"))
     if (rec and rec.get("kernel_source_hash") == kernel_source_hash()
             and rec.get("workload") == args.workload and rec.get("shared_mode") == shared_mode
+            and not args.input_block and T == counts[-1]
             and dominant in str(rec.get("kernel", ""))):
         traffic = rec.get("hbm_bytes_per_launch")
 
@@ -223,7 +228,8 @@ def main() -> int:
                    "tokens": T, "weights": shape.w_dtype, "accumulate": "fp32",
                    "layer_copies": L, "shared_mode": shared_mode,
                    "regime": "gemm" if dominant == "gg_gate_up" else "matvec",
-                   "launch": "eager" if args.eager else "hip_graph"},
+                   "launch": "eager" if args.eager else "hip_graph",
+                   "input_block": "rmsnorm+residual" if args.input_block else "none"},
         "expert_weight_GBps": round(gbps, 1),
         "expert_weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "unique_experts_per_step": round(unique_mean, 3),

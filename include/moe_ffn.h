@@ -105,6 +105,18 @@ typedef enum moe_ffn_dtype {
  * wrong stream.  They change timing only, never results. */
 #define MOE_FFN_DEBUG_DELAY_AUX 0x100u
 #define MOE_FFN_DEBUG_DELAY_MAIN 0x200u
+/* The decode block around the layer (page "ggml-cuda: overlap the MoE shared
+ * expert on a separate stream", its commit list: the FFN-input norm is the node
+ * both branches fork from, and the branches meet at an add; page "ggml operator
+ * extensions", section "sd.cpp integration": an RMSNorm followed by a multiply
+ * with a one-dimensional weight vector; each operation rounded separately):
+ *   INPUT_NORM  x -> (x * rho) * norm_weight, rho = 1/sqrt(mean(x^2) + norm_eps),
+ *               per token in fp32; the router takes it in fp32, the experts and
+ *               the shared expert in x_dtype (bf16 x: rounded to nearest even).
+ *   RESIDUAL    out = x + (routed + s * S), x the layer's input before any norm,
+ *               each operation rounded to fp32 separately. */
+#define MOE_FFN_INPUT_NORM 0x1000u
+#define MOE_FFN_RESIDUAL 0x2000u
 /* Test hook: in the mat-vec regime run the down step and the join as two
  * launches where one (MOE_FFN_K_DOWN_JOIN) would apply.  Results are
  * bit-identical either way. */
@@ -125,8 +137,10 @@ typedef struct moe_ffn_desc {
     int32_t device;             /* HIP device ordinal the plan runs on */
     int32_t x_dtype;            /* moe_ffn_dtype of x: F32 or BF16 */
     int32_t weight_dtype;       /* moe_ffn_dtype of every routed and shared FFN matrix */
-    uint32_t flags;             /* MOE_FFN_SHARED_*, MOE_FFN_FORCE_*, MOE_FFN_DEBUG_* */
+    uint32_t flags;             /* MOE_FFN_SHARED_*, MOE_FFN_FORCE_*, MOE_FFN_INPUT_NORM,
+                                   MOE_FFN_RESIDUAL, MOE_FFN_DEBUG_* */
     int32_t matvec_max_tokens;  /* regime switch; 0 = library default (6) */
+    float norm_eps;             /* INPUT_NORM epsilon (>= 0, finite); ignored otherwise */
 } moe_ffn_desc;
 
 /* Device pointers for one forward.  Row-major, contiguous, 16-byte aligned.
@@ -157,6 +171,7 @@ typedef struct moe_ffn_tensors {
     float *dbg_topk_weights;     /* [T, k] renormalised routing weights */
     float *dbg_logits;           /* [T, E] router logits */
     float *dbg_shared_gate;      /* [T] sigmoid gate of the shared expert */
+    const float *norm_weight;    /* [H] fp32: set exactly when desc.flags has INPUT_NORM */
 } moe_ffn_tensors;
 
 typedef struct moe_ffn_plan_s *moe_ffn_plan_t;

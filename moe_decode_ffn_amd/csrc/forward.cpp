@@ -134,6 +134,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     for (const void *p : sc)
         if ((p != nullptr) != q4)
             return set_error(MOE_FFN_ERR_INVALID_ARG, "scale pointers must be set exactly for Q4_B32 storage");
+    const bool norm = d.flags & MOE_FFN_INPUT_NORM;
+    if ((t->norm_weight != nullptr) != norm)
+        return set_error(MOE_FFN_ERR_INVALID_ARG, "norm_weight must be set exactly when INPUT_NORM is");
     if (!workspace) return set_error(MOE_FFN_ERR_INVALID_ARG, "workspace must not be NULL");
     if (workspace_bytes < P->L.total)
         return set_error(MOE_FFN_ERR_WORKSPACE_TOO_SMALL,
@@ -142,7 +145,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     const void *all[] = {t->x, t->w_router, t->w_gate, t->w_up, t->w_down, t->w_gate_scale,
                          t->w_up_scale, t->w_down_scale, t->sh_gate, t->sh_up, t->sh_down,
                          t->sh_gate_scale, t->sh_up_scale, t->sh_down_scale, t->gate_vec, t->out,
-                         t->dbg_topk_ids, t->dbg_topk_weights, t->dbg_logits, t->dbg_shared_gate};
+                         t->dbg_topk_ids, t->dbg_topk_weights, t->dbg_logits, t->dbg_shared_gate,
+                         t->norm_weight};
     for (const void *p : all)
         if (!aligned(p, 16)) return set_error(MOE_FFN_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
 
@@ -167,6 +171,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         {t->sh_up_scale, q4 ? Is * (H / 32) * 2 : 0},
         {t->sh_down_scale, q4 ? H * (Is / 32) * 2 : 0},
         {t->gate_vec, H * 4},
+        {t->norm_weight, norm ? H * 4 : 0},
         {workspace, P->L.total},
         {t->dbg_topk_ids, t->dbg_topk_ids ? T * k * 4 : 0},
         {t->dbg_topk_weights, t->dbg_topk_weights ? T * k * 4 : 0},
@@ -205,6 +210,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     int *pairs = (int *)(W + L.pairs), *pos_expert = (int *)(W + L.pos_expert);
     int *records = (int *)(W + L.records);
     float *logits = (float *)(W + L.logits), *h = (float *)(W + L.h), *y = (float *)(W + L.y);
+    // the experts' input: x, or the router's normalised copy of it
+    const void *xe = norm ? (const void *)(W + L.xn) : t->x;
+    const void *resid = (d.flags & MOE_FFN_RESIDUAL) ? t->x : nullptr;
 
     const uint32_t mode = n_tokens <= P->matvec_max ? P->mode_matvec : P->mode_gemm;
     const bool gemm = P->gemm_ok && ((d.flags & MOE_FFN_FORCE_GEMM) || n_tokens > P->matvec_max);
@@ -228,9 +236,10 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
     rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
     rp.tickets = P->tickets;
+    rp.norm_w = t->norm_weight; rp.norm_eps = d.norm_eps; rp.xn = W + L.xn;
 
     GateUpParams gp{};
-    gp.x = t->x; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
+    gp.x = xe; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
     gp.x_resident = (size_t)Ti * H * xb <= kStageBytes ? 1 : 0;
     gp.tok_per_pass = std::max(1, (int)(kStageBytes / (H * xb)));
     gp.wg = (const uint8_t *)t->w_gate; gp.wu = (const uint8_t *)t->w_up;
@@ -273,7 +282,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
 
     // grouped-GEMM regime: h is kept in bf16 (the down GEMM's operand) in the same regions
     GGParams gg{};
-    gg.x = t->x; gg.T = Ti; gg.H = (int)H; gg.k = (int)k; gg.E = (int)E; gg.I = (int)I;
+    gg.x = xe; gg.T = Ti; gg.H = (int)H; gg.k = (int)k; gg.E = (int)E; gg.I = (int)I;
     gg.Is = (int)Is; gg.records = records; gg.n_unique = n_unique; gg.pairs = pairs;
     gg.hb = (uint16_t *)h; gg.shb = (uint16_t *)sh_h; gg.y = y; gg.S = sh_S;
     const int gg_rows = gg_rows_per_job();
@@ -291,10 +300,12 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     djp.pairs = pairs; djp.pos_expert = pos_expert;
     djp.swd = (const uint8_t *)t->sh_down; djp.ssd = t->sh_down_scale; djp.Is = (int)Is; djp.hs = sh_h;
     djp.S = sh_S; djp.wts = wts; djp.gate_s = gate_s; djp.out = t->out;
+    djp.resid = resid; djp.resid_bf16 = d.x_dtype == MOE_FFN_BF16;
 
     JoinParams jp{};
     jp.T = Ti; jp.H = (int)H; jp.k = (int)k; jp.y = y; jp.wts = wts; jp.gate_s = gate_s;
     jp.S = sh_S; jp.out = t->out;
+    jp.resid = resid; jp.resid_bf16 = d.x_dtype == MOE_FFN_BF16;
 
     const bool delay_main = d.flags & MOE_FFN_DEBUG_DELAY_MAIN;
     const bool delay_aux = d.flags & MOE_FFN_DEBUG_DELAY_AUX;
@@ -382,14 +393,22 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         return timed(P, MOE_FFN_K_DOWN_JOIN, s, [&] { return launch_down_join(q, wk, P->map_down, s); });
     };
     if (mode == MOE_FFN_SHARED_AUX) {
+        // the shared branch reads the experts' input: with the input norm it forks
+        // after the router launch that writes it, else at entry
+        if (norm) {
+            if (delay_main) chk(launch_delay(stream, delay_ticks));
+            chk(run_router(stream));
+        }
         chk(hipEventRecord(P->ev_fork, stream));
         chk(hipStreamWaitEvent(P->aux, P->ev_fork, 0));
         if (delay_aux) chk(launch_delay(P->aux, delay_ticks));
         chk(step_gate_up(P->aux, false, true));
         chk(step_down(P->aux, false, true));
         chk(hipEventRecord(P->ev_join, P->aux));
-        if (delay_main) chk(launch_delay(stream, delay_ticks));
-        chk(run_router(stream));
+        if (!norm) {
+            if (delay_main) chk(launch_delay(stream, delay_ticks));
+            chk(run_router(stream));
+        }
         chk(step_gate_up(stream, true, false));
         if (use_dj) {  // the fused launch reads S: wait for the shared branch first
             chk(hipStreamWaitEvent(stream, P->ev_join, 0));
@@ -400,11 +419,12 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
             chk(run_join(stream));
         }
     } else if (mode == MOE_FFN_SHARED_SEQ) {
+        if (norm) chk(run_router(stream));  // writes the experts' input
         if (delay_aux) chk(launch_delay(stream, delay_ticks));
         chk(step_gate_up(stream, false, true));
         chk(step_down(stream, false, true));
         if (delay_main) chk(launch_delay(stream, delay_ticks));
-        chk(run_router(stream));
+        if (!norm) chk(run_router(stream));
         chk(step_gate_up(stream, true, false));
         chk(run_tail(stream, false));
     } else {  // FUSED

@@ -53,6 +53,7 @@ struct Layout {
     size_t pairs = 0;      // i32 [Tmax*k]: pair id t*k+j in expert-bucketed order
     size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
     size_t logits = 0;     // f32 [Tmax][E+1] (column E = shared-gate logit), router -> gate/up
+    size_t xn = 0;         // x_dtype [Tmax][H]: normalised input (INPUT_NORM), router -> experts
     size_t routing_bytes = 0;
     // phase region: reused by the sequential steps
     size_t h = 0;       // gate/up -> down: f32 [Tmax*k][I]
@@ -121,6 +122,10 @@ struct RouterParams {
     float *dbg_w, *dbg_logits, *dbg_gate;
     unsigned *tickets;      // plan memory: [kMaxTokens] per token tile + [1] across tiles, zero between calls
     int route_tail;         // 1: the launch also ranks and buckets (else k_route or the gate/up launch)
+    // input RMSNorm: logits from the normalised tokens; workgroup column 0 writes them for the experts
+    const float *norm_w;    // [H] or NULL: no norm
+    float norm_eps;
+    void *xn;               // [T][H] x_dtype
 };
 
 struct GateUpParams {
@@ -195,6 +200,8 @@ struct DownJoinParams {
     const float *wts;       // [T*k]
     const float *gate_s;    // [T]
     float *out;             // [T][H]
+    const void *resid;      // [T][H] x_dtype: the residual input, or NULL
+    int resid_bf16;
 };
 
 struct GGParams {
@@ -213,6 +220,8 @@ struct GGParams {
 };
 
 struct JoinParams {
+    const void *resid;   // [T][H] x_dtype: the residual input, or NULL
+    int resid_bf16;
     int T, H, k;
     const float *y;      // [T*k][H]
     const float *wts;    // [T*k]

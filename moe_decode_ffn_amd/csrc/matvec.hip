@@ -497,6 +497,12 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
     }
 }
 
+// the block's residual input, decoded to fp32 (exact for bf16)
+__device__ __forceinline__ float resid_at(const void *x, int is_bf16, size_t i) {
+    return is_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[i] << 16)
+                   : reinterpret_cast<const float *>(x)[i];
+}
+
 // ---- down + join: one workgroup per tile of output rows (small batches) ---------------------
 constexpr int kDJWaves = 16;
 
@@ -604,7 +610,9 @@ __global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
         float routed = wt[0] * yt[0];
         for (int j = 1; j < k; ++j) routed = fmaf(wt[j], yt[(size_t)j * RT], routed);
         const float S = p.shared_here ? s_y[(size_t)(NP + t) * RT + rr] : p.S[(size_t)t * H + r];
-        p.out[(size_t)t * H + r] = __fadd_rn(routed, __fmul_rn(s_g[t], S));
+        float o = __fadd_rn(routed, __fmul_rn(s_g[t], S));
+        if (p.resid) o = __fadd_rn(resid_at(p.resid, p.resid_bf16, (size_t)t * H + r), o);
+        p.out[(size_t)t * H + r] = o;
     }
 }
 
@@ -628,7 +636,9 @@ __global__ __launch_bounds__(256) void k_join(JoinParams p) {
 #pragma unroll
     for (int j = 1; j < kMaxTopK; ++j)
         if (j < k) routed = fmaf(wv[j], yv[j], routed);
-    p.out[(size_t)t * p.H + r] = __fadd_rn(routed, __fmul_rn(p.gate_s[t], S));
+    float o = __fadd_rn(routed, __fmul_rn(p.gate_s[t], S));
+    if (p.resid) o = __fadd_rn(resid_at(p.resid, p.resid_bf16, (size_t)t * p.H + r), o);
+    p.out[(size_t)t * p.H + r] = o;
 }
 
 // ---- launchers ----------------------------------------------------------------------------

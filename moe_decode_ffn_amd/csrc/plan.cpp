@@ -87,8 +87,11 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     if (!desc || !out_plan) return set_error(MOE_FFN_ERR_INVALID_ARG, "desc and out_plan must not be NULL");
     const moe_ffn_desc d = *desc;
     const uint32_t known = MOE_FFN_SHARED_MASK | MOE_FFN_FORCE_MATVEC | MOE_FFN_FORCE_GEMM |
-                           MOE_FFN_DEBUG_DELAY_AUX | MOE_FFN_DEBUG_DELAY_MAIN | MOE_FFN_DEBUG_SPLIT_JOIN;
+                           MOE_FFN_DEBUG_DELAY_AUX | MOE_FFN_DEBUG_DELAY_MAIN | MOE_FFN_DEBUG_SPLIT_JOIN |
+                           MOE_FFN_INPUT_NORM | MOE_FFN_RESIDUAL;
     if (d.flags & ~known) return set_error(MOE_FFN_ERR_INVALID_ARG, "unknown flag bits");
+    if ((d.flags & MOE_FFN_INPUT_NORM) && !(d.norm_eps >= 0.f && d.norm_eps <= 3.4e38f))
+        return set_error(MOE_FFN_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
     if ((d.flags & MOE_FFN_FORCE_MATVEC) && (d.flags & MOE_FFN_FORCE_GEMM))
         return set_error(MOE_FFN_ERR_INVALID_ARG, "FORCE_MATVEC and FORCE_GEMM are exclusive");
     if (d.hidden <= 0 || d.n_experts <= 0 || d.top_k <= 0 || d.inter <= 0 || d.shared_inter <= 0 ||
@@ -158,6 +161,8 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.pairs = c;      c += align_up(P_ * 4);
     L.pos_expert = c; c += align_up(P_ * 4);
     L.logits = c;     c += align_up(T * (E + 1) * 4);
+    // normalised input of both branches (x_dtype), router -> experts
+    L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
     L.routing_bytes = c - L.shared_bytes;
     // sequential steps: gate/up holds h, down holds h and y, join holds y
     const size_t base = c;

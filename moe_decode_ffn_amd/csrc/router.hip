@@ -71,18 +71,53 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
+    // input RMSNorm folded into the dot products: logit = rho * sum_h (W[h] * g[h]) * x[h],
+    // rho = 1/sqrt(mean(x^2) + eps), the squares summed alongside (the same lanes and
+    // order in every workgroup, so every workgroup gets the same rho bits).  The norm
+    // weights are fetched with the rows and folded in once the tokens are staged, so
+    // that no load waits for another
+    const bool norm = p.norm_w != nullptr;
+    float4 gn[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = sl + LPR * n;
+        gn[n] = (norm && c < n_chunks) ? *reinterpret_cast<const float4 *>(p.norm_w + 4 * c)
+                                       : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+
     const int t0 = blockIdx.y * p.tok_tile;
     const int nt = min(p.tok_tile, p.T - t0);
+    // the normalised tokens of the tile are written by the column's workgroups in
+    // order, one 4-element chunk per thread and pass; the first chunk's norm weights
+    // are fetched now as well
+    const int xn_units = norm ? nt * n_chunks : 0;
+    const int xn_u0 = blockIdx.x * 256 + tid;
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (xn_u0 < xn_units) g0 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * (xn_u0 % n_chunks));
     const int xrow = H * (XBF ? 2 : 4);
     const uint8_t *xs = (const uint8_t *)p.x + (size_t)t0 * xrow;
     for (int i = tid; i < nt * xrow / 16; i += 256)
         reinterpret_cast<uint4 *>(lds)[i] = ld16(xs + 16 * (size_t)i);
     __syncthreads();
+    if (norm) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            w[n] = make_float4(w[n].x * gn[n].x, w[n].y * gn[n].y, w[n].z * gn[n].z, w[n].w * gn[n].w);
+    }
+
+    auto x_chunk = [&](int i, int c) -> float4 {
+        if constexpr (XBF) {
+            const uint2 b = *reinterpret_cast<const uint2 *>(lds + i * xrow + 8 * c);
+            return make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+        } else {
+            return *reinterpret_cast<const float4 *>(lds + i * xrow + 16 * c);
+        }
+    };
 
     // partial dot products of up to 8 tokens, then one transposed reduction for all
-    float acc[kRouterTile];
+    float acc[kRouterTile], ss[kRouterTile];
 #pragma unroll
-    for (int i = 0; i < kRouterTile; ++i) acc[i] = 0.f;
+    for (int i = 0; i < kRouterTile; ++i) acc[i] = ss[i] = 0.f;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
         const int c = sl + LPR * n;
@@ -90,24 +125,59 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
 #pragma unroll
             for (int i = 0; i < kRouterTile; ++i) {
                 if (i < nt) {
-                    float4 xv;
-                    if constexpr (XBF) {
-                        const uint2 b = *reinterpret_cast<const uint2 *>(lds + i * xrow + 8 * c);
-                        xv = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
-                    } else {
-                        xv = *reinterpret_cast<const float4 *>(lds + i * xrow + 16 * c);
-                    }
+                    const float4 xv = x_chunk(i, c);
                     acc[i] = fmaf(w[n].x, xv.x, acc[i]);
                     acc[i] = fmaf(w[n].y, xv.y, acc[i]);
                     acc[i] = fmaf(w[n].z, xv.z, acc[i]);
                     acc[i] = fmaf(w[n].w, xv.w, acc[i]);
+                    if (norm) {
+                        ss[i] = fmaf(xv.x, xv.x, ss[i]);
+                        ss[i] = fmaf(xv.y, xv.y, ss[i]);
+                        ss[i] = fmaf(xv.z, xv.z, ss[i]);
+                        ss[i] = fmaf(xv.w, xv.w, ss[i]);
+                    }
                 }
             }
         }
     }
     int tok = 0;
-    const float sum = seg_sum8<LPR>(acc, sl, tok);
-    if (valid && (sl & (LPR / 8 - 1)) == 0 && tok < nt) p.logits[(size_t)(t0 + tok) * (E + 1) + row] = sum;
+    float sum = seg_sum8<LPR>(acc, sl, tok);
+    const bool writer = (sl & (LPR / 8 - 1)) == 0 && tok < nt;
+    float rho = 1.f;
+    if (norm) {
+        const float sq = seg_sum8<LPR>(ss, sl, tok);
+        rho = 1.0f / sqrtf(sq / (float)H + p.norm_eps);
+        sum *= rho;
+    }
+    if (valid && writer) p.logits[(size_t)(t0 + tok) * (E + 1) + row] = sum;
+    if (norm) {
+        // the normalised tokens, (x * rho) * g, that feed both expert branches, rounded
+        // to the activation storage
+        if (blockIdx.x * 256 < xn_units) {
+            __shared__ float s_rho[kRouterTile];
+            if (wave == 0 && seg == 0 && writer) s_rho[tok] = rho;
+            __syncthreads();
+            for (int q = xn_u0; q < xn_units; q += 256 * gridDim.x) {
+                const int i = q / n_chunks, c = q - i * n_chunks;
+                const float r = s_rho[i];
+                const float4 xv = x_chunk(i, c);
+                const float4 g = q == xn_u0 ? g0 : *reinterpret_cast<const float4 *>(p.norm_w + 4 * c);
+                const float v0 = __fmul_rn(__fmul_rn(xv.x, r), g.x), v1 = __fmul_rn(__fmul_rn(xv.y, r), g.y);
+                const float v2 = __fmul_rn(__fmul_rn(xv.z, r), g.z), v3 = __fmul_rn(__fmul_rn(xv.w, r), g.w);
+                const size_t o = (size_t)(t0 + i) * H + 4 * c;
+                if constexpr (XBF) {
+                    uint2 b;
+                    b.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
+                    b.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.xn) + o) = b;
+                } else {
+                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.xn) + o) = make_float4(v0, v1, v2, v3);
+                }
+            }
+        }
+    }
 
     // ---- routing tail ----
     if (!p.route_tail) return;

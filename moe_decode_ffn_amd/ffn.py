@@ -24,6 +24,7 @@ F32, BF16, Q4_B32 = 0, 1, 2
 # flags
 SHARED_AUTO, SHARED_AUX, SHARED_SEQ, SHARED_FUSED, SHARED_MASK = 0x0, 0x1, 0x2, 0x3, 0x3
 FORCE_MATVEC, FORCE_GEMM = 0x10, 0x20
+INPUT_NORM, RESIDUAL = 0x1000, 0x2000
 DEBUG_DELAY_AUX, DEBUG_DELAY_MAIN, DEBUG_SPLIT_JOIN = 0x100, 0x200, 0x400
 # moe_ffn_kernel_id
 KERNELS = ("router", "route", "gate_up", "down", "sh_gate_up", "sh_down", "join", "gg_gate_up",
@@ -45,7 +46,7 @@ class Desc(ctypes.Structure):
                 ("shared_inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("matvec_max_tokens", ctypes.c_int32)]
+                ("matvec_max_tokens", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -56,7 +57,7 @@ class Tensors(ctypes.Structure):
         "x", "w_router", "w_gate", "w_up", "w_down", "w_gate_scale", "w_up_scale",
         "w_down_scale", "sh_gate", "sh_up", "sh_down", "sh_gate_scale", "sh_up_scale",
         "sh_down_scale", "gate_vec", "out", "dbg_topk_ids", "dbg_topk_weights", "dbg_logits",
-        "dbg_shared_gate")]
+        "dbg_shared_gate", "norm_weight")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -167,19 +168,31 @@ class MoeFfn:
     """A plan plus the bookkeeping to call it with torch tensors.
 
     ``layer`` dicts use the keys router, gate, up, down, sh_gate, sh_up, sh_down,
-    gate_vec and, for 4-bit storage, <name>_scale.
+    gate_vec and, for 4-bit storage, <name>_scale; with the INPUT_NORM flag also
+    norm_w (fp32 [H]).
     """
 
     def __init__(self, hidden, n_experts, top_k, inter, shared_inter, max_tokens, x_dtype="bf16",
-                 w_dtype="bf16", flags=SHARED_AUTO, device=0, matvec_max_tokens=0):
+                 w_dtype="bf16", flags=SHARED_AUTO, device=0, matvec_max_tokens=0, norm_eps=0.0):
         self.desc = Desc(hidden, n_experts, top_k, inter, shared_inter, max_tokens, device,
-                         DTYPES[x_dtype], DTYPES[w_dtype], flags, matvec_max_tokens)
+                         DTYPES[x_dtype], DTYPES[w_dtype], flags, matvec_max_tokens, norm_eps)
         self.plan, self.workspace_bytes = moe_ffn_plan(self.desc)
 
     @classmethod
     def for_shape(cls, shape, max_tokens, **kw):
         return cls(shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter,
                    max_tokens, shape.x_dtype, shape.w_dtype, **kw)
+
+    @classmethod
+    def for_layer(cls, layer: dict, max_tokens, flags=SHARED_AUTO, **kw):
+        """A plan for a layer dict; its norm_w / norm_eps / residual keys add the
+        INPUT_NORM / RESIDUAL flags and the eps."""
+        if layer.get("norm_w") is not None:
+            flags |= INPUT_NORM
+            kw.setdefault("norm_eps", float(layer.get("norm_eps", 0.0)))
+        if layer.get("residual"):
+            flags |= RESIDUAL
+        return cls.for_shape(layer["shape"], max_tokens, flags=flags, **kw)
 
     def info(self) -> PlanInfo:
         return moe_ffn_plan_get_info(self.plan)
@@ -205,7 +218,7 @@ class MoeFfn:
             _ptr(layer["sh_down"]), _ptr(layer.get("sh_gate_scale")),
             _ptr(layer.get("sh_up_scale")), _ptr(layer.get("sh_down_scale")),
             _ptr(layer["gate_vec"]), _ptr(out), _ptr(dbg.get("ids")), _ptr(dbg.get("weights")),
-            _ptr(dbg.get("logits")), _ptr(dbg.get("gate")))
+            _ptr(dbg.get("logits")), _ptr(dbg.get("gate")), _ptr(layer.get("norm_w")))
 
     def forward(self, layer: dict, x, out, workspace, stream=None, dbg: Optional[dict] = None,
                 n_tokens: Optional[int] = None) -> None:

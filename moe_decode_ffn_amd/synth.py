@@ -13,7 +13,8 @@ layer of the same shapes):
   nearest-even bf16, or 4-bit symmetric blocks: integer q uniform in [-8, 7],
   one fp16 scale per 32-element block drawn U(0.001, 0.01) in fp32 then
   rounded to fp16;
-* tokens: i.i.d. N(0, 1), stored as bf16 (or fp32 for the all-fp32 layer).
+* tokens: i.i.d. N(0, 1), stored as bf16 (or fp32 for the all-fp32 layer);
+* the optional input-norm weights: U(0.5, 1.5), fp32.
 
 4-bit block layout ("Q4_B32"): a block is 32 consecutive elements along the
 input (reduction) dimension of a weight row.  Element j of a block lives in
@@ -42,6 +43,11 @@ Q4_SCALE_HI = 0.01
 # matrix ids used in the per-expert spawn keys (fixed generation order)
 _MID_ROUTER, _MID_GATE, _MID_UP, _MID_DOWN = 0, 1, 2, 3
 _MID_SH_GATE, _MID_SH_UP, _MID_SH_DOWN, _MID_GVEC, _MID_X = 4, 5, 6, 7, 8
+_MID_NORM = 9
+
+# weights of the optional input RMSNorm: U(0.5, 1.5), fp32 (a trained norm's
+# per-channel gains sit around one)
+NORM_W_LO, NORM_W_HI = 0.5, 1.5
 
 
 @dataclass(frozen=True)
@@ -154,6 +160,26 @@ def make_layer(shape: LayerShape, seed: int) -> dict:
         layer[name + "_scale"] = None if s is None else s.contiguous()
     layer["gate_vec"] = torch.from_numpy(_normal_f32(seed, _MID_GVEC, 1, 1, H, WEIGHT_STD)[0, 0])
     return layer
+
+
+def make_norm_weight(shape: LayerShape, seed: int) -> torch.Tensor:
+    """[H] fp32 weights of the input RMSNorm, U(0.5, 1.5)."""
+    g = _stream(seed, _MID_NORM, 0)
+    return torch.from_numpy(g.uniform(NORM_W_LO, NORM_W_HI, shape.hidden).astype(np.float32))
+
+
+def with_input_block(layer: dict, seed: int, eps: float = 1e-6, norm: bool = True,
+                     residual: bool = True) -> dict:
+    """A copy of `layer` that also carries the input RMSNorm (norm_w, norm_eps)
+    and/or the residual add (the keys the binding and the oracle read)."""
+    out = dict(layer)
+    if norm:
+        w = make_norm_weight(layer["shape"], seed)
+        dev = layer["gate_vec"].device
+        out["norm_w"] = w.to(dev)
+        out["norm_eps"] = float(eps)
+    out["residual"] = bool(residual)
+    return out
 
 
 def make_tokens(shape: LayerShape, n_tokens: int, seed: int, stream: int = 0) -> torch.Tensor:

@@ -37,7 +37,8 @@ def oracle_layer(layer: dict) -> OracleLayer:
         gate_scale=stored(layer["gate_scale"]), up_scale=stored(layer["up_scale"]),
         down_scale=stored(layer["down_scale"]), sh_gate_scale=stored(layer["sh_gate_scale"]),
         sh_up_scale=stored(layer["sh_up_scale"]), sh_down_scale=stored(layer["sh_down_scale"]),
-        norm_w=stored(layer.get("norm_w")), norm_eps=float(layer.get("norm_eps", 0.0)),
+        # the plan takes eps as fp32: the oracle gets that same value
+        norm_w=stored(layer.get("norm_w")), norm_eps=float(np.float32(layer.get("norm_eps", 0.0))),
         residual=bool(layer.get("residual", False)))
 
 

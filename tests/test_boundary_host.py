@@ -67,7 +67,8 @@ def test_status_strings(lib):
 
 def desc(**kw):
     base = dict(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, max_tokens=8,
-                device=0, x_dtype=ffn.BF16, weight_dtype=ffn.BF16, flags=0, matvec_max_tokens=0)
+                device=0, x_dtype=ffn.BF16, weight_dtype=ffn.BF16, flags=0, matvec_max_tokens=0,
+                norm_eps=0.0)
     base.update(kw)
     return ffn.Desc(**base)
 
@@ -138,6 +139,35 @@ def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     assert ws == info.workspace_bytes == shared + routing + max(phases.values())
 
 
+@pytest.mark.parametrize("x_dtype,w_dtype,xb", [(ffn.BF16, ffn.BF16, 2), (ffn.F32, ffn.F32, 4)])
+def test_workspace_with_input_norm(lib, x_dtype, w_dtype, xb):
+    # the normalised tokens (x_dtype) join the routing region; nothing else changes
+    T, H = 8, 2048
+    p0, ws0 = ffn.moe_ffn_plan(desc(max_tokens=T, x_dtype=x_dtype, weight_dtype=w_dtype))
+    p1, ws1 = ffn.moe_ffn_plan(desc(max_tokens=T, x_dtype=x_dtype, weight_dtype=w_dtype,
+                                    flags=ffn.INPUT_NORM | ffn.RESIDUAL, norm_eps=1e-6))
+    i0, i1 = ffn.moe_ffn_plan_get_info(p0), ffn.moe_ffn_plan_get_info(p1)
+    ffn.moe_ffn_destroy(p0)
+    ffn.moe_ffn_destroy(p1)
+    assert i1.routing_region_bytes == i0.routing_region_bytes + _align(T * H * xb)
+    assert i1.shared_region_bytes == i0.shared_region_bytes
+    assert i1.phase_region_bytes == i0.phase_region_bytes
+    assert ws1 == ws0 + _align(T * H * xb)
+    p2, ws2 = ffn.moe_ffn_plan(desc(max_tokens=T, x_dtype=x_dtype, weight_dtype=w_dtype,
+                                    flags=ffn.RESIDUAL))
+    ffn.moe_ffn_destroy(p2)
+    assert ws2 == ws0  # the residual add needs no scratch
+
+
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf"), -float("inf")])
+def test_plan_rejects_bad_norm_eps(lib, eps):
+    with pytest.raises(ffn.MoeFfnError) as e:
+        ffn.moe_ffn_plan(desc(flags=ffn.INPUT_NORM, norm_eps=eps))
+    assert e.value.status == ffn.ERR_INVALID_ARG
+    p, _ = ffn.moe_ffn_plan(desc(flags=ffn.INPUT_NORM, norm_eps=0.0))  # eps 0 is allowed
+    ffn.moe_ffn_destroy(p)
+
+
 def test_auto_mode_defaults(lib):
     plan, _ = ffn.moe_ffn_plan(desc())
     info = ffn.moe_ffn_plan_get_info(plan)
@@ -205,6 +235,28 @@ def test_forward_validation(lib, plan):
     assert _fwd(lib, p, g.t, 1, g.ws, wsb) == ffn.ERR_INVALID_ARG
     g = FakeTensors(q4=True)  # scales on a bf16 plan
     assert _fwd(lib, p, g.t, 1, g.ws, wsb) == ffn.ERR_INVALID_ARG
+
+
+def test_forward_validation_input_norm(lib, plan):
+    p, wsb = plan
+    f = FakeTensors()
+    f.t.norm_weight = f.alloc()  # a norm weight on a plan without INPUT_NORM
+    assert _fwd(lib, p, f.t, 1, f.ws, wsb) == ffn.ERR_INVALID_ARG
+    pn, wsn = ffn.moe_ffn_plan(desc(flags=ffn.INPUT_NORM | ffn.RESIDUAL, norm_eps=1e-6))
+    try:
+        g = FakeTensors()  # INPUT_NORM without a norm weight
+        assert _fwd(lib, pn, g.t, 1, g.ws, wsn) == ffn.ERR_INVALID_ARG
+        g.t.norm_weight = g.alloc() + 4
+        assert _fwd(lib, pn, g.t, 1, g.ws, wsn) == ffn.ERR_MISALIGNED
+        g = FakeTensors()
+        g.t.norm_weight = g.alloc()
+        g.t.out = g.t.norm_weight  # out over the norm weight
+        assert _fwd(lib, pn, g.t, 2, g.ws, wsn) == ffn.ERR_ALIAS
+        g = FakeTensors()
+        g.t.norm_weight = g.alloc()
+        assert _fwd(lib, pn, g.t, 1, g.ws, wsn - 1) == ffn.ERR_WORKSPACE_TOO_SMALL
+    finally:
+        ffn.moe_ffn_destroy(pn)
 
 
 def test_forward_aliasing(lib, plan):
