@@ -23,6 +23,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBRARY = os.path.join(LIBDIR, "libmoe_ffn.so")
 DRIVER_SRC = os.path.join(PKG, "driver", "layer_loop.hip")
 DRIVER = os.path.join(LIBDIR, "layer_loop")
+BARRIER_SRC = os.path.join(PKG, "driver", "grid_barrier.hip")
+BARRIER = os.path.join(LIBDIR, "grid_barrier")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -63,13 +65,20 @@ def build_library(jobs: int | None = None) -> str:
 
 
 def build_driver() -> str:
-    """layer_loop, linked against the in-tree library (found next to it at run time)."""
+    """layer_loop, linked against the in-tree library (found next to it at run time), and
+    grid_barrier."""
     tmp = DRIVER + ".tmp"
     cmd = [HIPCC, *COMMON, DRIVER_SRC, "-o", tmp, f"-L{LIBDIR}", "-lmoe_ffn", "-Wl,-rpath,$ORIGIN"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {DRIVER_SRC}:\n{r.stderr}")
     os.replace(tmp, DRIVER)
+    # the grid-barrier cost driver (stand-alone: no library)
+    tmp = BARRIER + ".tmp"
+    r = subprocess.run([HIPCC, *COMMON, BARRIER_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {BARRIER_SRC}:\n{r.stderr}")
+    os.replace(tmp, BARRIER)
     return DRIVER
 
 
