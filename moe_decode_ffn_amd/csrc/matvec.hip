@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     if (route_here) {
         // every workgroup ranks and buckets the whole batch; workgroup 0 publishes
         uint8_t *area = lds + p.route_lds_off;
-        const RouteLds L = route_lds_layout(T, k, p.E, kWaves, true);
+        const RouteLds L = route_lds_layout(T, k, p.E, true);
         const bool pub = blockIdx.x == 0;
         RouteGlobal g{};
         if (pub) g = RouteGlobal{p.ids, p.wts, p.gate_s, const_cast<int *>(p.records),
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(256) void k_join(JoinParams p) {
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes) {
     const int toks = p.x_resident ? p.T : p.tok_per_pass;
     const size_t stage = ((size_t)toks * p.H * xbytes + 15) & ~(size_t)15;
-    return stage + (p.routed && p.route_here ? route_lds_layout(p.T, p.k, p.E, kWaves, true).bytes : 0);
+    return stage + (p.routed && p.route_here ? route_lds_layout(p.T, p.k, p.E, true).bytes : 0);
 }
 
 int gate_up_route_lds_off(const GateUpParams &p, int xbytes) {

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
     if (!p.route_tail) return;
     if (!last_arrival(p.tickets + blockIdx.y, gridDim.x)) return;
     const int T = p.T, k = p.k;
-    const RouteLds L = route_lds_layout(T, k, E, kRouterWaves, false);
+    const RouteLds L = route_lds_layout(T, k, E, false);
     const bool one_tile = gridDim.y == 1;
     const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
                         p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
@@ -196,13 +196,13 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
     bucket_tokens(T, k, E, lds, L, g);
 }
 
-size_t route_lds_bytes(int T, int k, int E) { return route_lds_layout(T, k, E, kRouterWaves, false).bytes; }
+size_t route_lds_bytes(int T, int k, int E) { return route_lds_layout(T, k, E, false).bytes; }
 
 // k_route: one workgroup, one wave per token (up to 16), ranks the batch and
 // buckets it (mid-size batches, between in-gate/up routing and the router tail).
 __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const RouteLds L = route_lds_layout(p.T, p.k, p.E, blockDim.x >> 6, false);
+    const RouteLds L = route_lds_layout(p.T, p.k, p.E, false);
     const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
                         p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
     rank_tokens(p.logits, 0, p.T, p.E, p.k, lds, L, g, false);
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
 int route_kernel_waves(int T) { return T < 4 ? 4 : T > 16 ? 16 : T; }
 
 size_t route_kernel_lds_bytes(int T, int k, int E) {
-    return route_lds_layout(T, k, E, route_kernel_waves(T), false).bytes;
+    return route_lds_layout(T, k, E, false).bytes;
 }
 
 hipError_t launch_route(const RouterParams &p, hipStream_t s) {

@@ -28,112 +28,76 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// LDS words one wave needs for ranking: key, index, value of up to kMaxTopK
-// picks (16-byte aligned).
-constexpr int kRankWords = 3 * 32;
+// Largest key over the wave, in every lane: a max butterfly inside each row of
+// 16 lanes (DPP), then the four row maxima read as scalars.
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xf, 0xf, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
 
-// One wave ranks one token.  lg: E+1 logits (column E = shared-gate logit);
-// wlds: kRankWords words of 16-byte-aligned LDS owned by this wave.
-//   1. radix select: the k-th largest key P, two bits at a time from the top,
-//      counting keys >= candidate with one ballot per element slot;
-//   2. selected = keys above P, plus the lowest-index keys equal to P until k;
-//   3. the k picks are compacted into LDS and lane j < k ranks pick j against
-//      the others (key descending, index ascending) -> its slot.
+// One wave ranks one token.  lg: E+1 logits (column E = shared-gate logit).
+// Expert e = lane * EPL + i sits in register slot i of its lane.  The k picks
+// are taken one per round in rank order: the largest remaining key over the
+// wave; among equal keys the lowest lane, and in it the lowest slot, which is
+// the lowest expert index.  The winner drops the pick and lane r keeps pick r.
+// Keys of real logits are at least 1 (0 marks a taken or padding slot), so the
+// picks are k distinct experts whatever the logits hold.
 // Weights: p_e = exp(l_e - max l) / sum_all exp(.) renormalised over the picks
 // is w_j = exp(l_j - m) / sum_picks exp(l_i - m) for any m (the full sum
-// cancels); m = the largest pick, which is also the largest logit.
+// cancels); m = the first pick, the largest logit.
 template <int EPL>
-__device__ void route_token(const float *lg, int E, int k, int lane, uint32_t *wlds, const RouteOut &o) {
+__device__ void route_token(const float *lg, int E, int k, int lane, const RouteOut &o) {
     float v[EPL];
     uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
         v[i] = e < E ? lg[e] : -INFINITY;
-        key[i] = e < E ? logit_key(v[i]) : 0u;  // padding sorts below every logit
+        key[i] = e < E ? max(logit_key(v[i]), 1u) : 0u;
     }
     const float glog = lg[E];
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = max(best, key[i]);
 
-    // 1. k-th largest key, two bits per round (three independent counts)
-    uint32_t P = 0;
-    for (int b = 30; b >= 0; b -= 2) {
-        const uint32_t c1 = P | (1u << b), c2 = P | (2u << b), c3 = P | (3u << b);
-        int n1 = 0, n2 = 0, n3 = 0;
+    int my_id = 0;
+    float my_v = 0.f;
+    for (int r = 0; r < k; ++r) {
+        const uint32_t M = wave_max_key(best);
+        const int win = (int)__builtin_ctzll(__ballot(best == M));
+        int wi = 0;
+        float wv = v[0];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            n1 += __popcll(__ballot(key[i] >= c1));
-            n2 += __popcll(__ballot(key[i] >= c2));
-            n3 += __popcll(__ballot(key[i] >= c3));
-        }
-        P = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : P;
-    }
-    // 2. selection: everything above P, then ties at P in index order
-    int above = 0;
-    unsigned long long eqm[EPL];
+        for (int i = EPL - 1; i >= 0; --i)
+            if (key[i] == M) { wi = i; wv = v[i]; }
+        const int slot = __builtin_amdgcn_readlane(wi, win);
+        const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), win));
+        if (lane == win) {
+            best = 0u;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        above += __popcll(__ballot(key[i] > P));
-        eqm[i] = __ballot(key[i] == P);
-    }
-    const int need = k - above;  // >= 1
-    const unsigned long long below = (1ull << lane) - 1ull;
-    int eq_before = 0;  // ties at P with a lower index than this lane's first slot
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) eq_before += __popcll(eqm[i] & below);
-    bool sel[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const bool eq = key[i] == P;
-        sel[i] = key[i] > P || (eq && eq_before < need);
-        eq_before += eq ? 1 : 0;
-    }
-    // 3. compaction in index order, then rank among the picks
-    int pos = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) pos += __popcll(__ballot(sel[i]) & below);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        if (sel[i]) {
-            wlds[pos] = key[i];
-            wlds[32 + pos] = (uint32_t)(lane * EPL + i);
-            wlds[64 + pos] = __float_as_uint(v[i]);
-            ++pos;
-        }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float myp = 0.f;
-    int myid = 0, slot = 0;
-    if (lane < k) {
-        const uint32_t mk = wlds[lane], mi = wlds[32 + lane];
-        const uint4 *k4 = reinterpret_cast<const uint4 *>(wlds);
-        const uint4 *i4 = reinterpret_cast<const uint4 *>(wlds + 32);
-        const uint4 *v4 = reinterpret_cast<const uint4 *>(wlds + 64);
-        float m = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (4 * q < k) {
-                const uint4 kk = k4[q], ii = i4[q], vv = v4[q];
-                const uint32_t ka[4] = {kk.x, kk.y, kk.z, kk.w}, ia[4] = {ii.x, ii.y, ii.z, ii.w};
-                const uint32_t va[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * q + r < k) {
-                        slot += (ka[r] > mk || (ka[r] == mk && ia[r] < mi)) ? 1 : 0;
-                        m = fmaxf(m, __uint_as_float(va[r]));
-                    }
+            for (int i = 0; i < EPL; ++i) {
+                if (i == slot) key[i] = 0u;
+                best = max(best, key[i]);
             }
         }
-        myid = (int)mi;
-        myp = expf(__uint_as_float(wlds[64 + lane]) - m);
+        if (lane == r) { my_id = win * EPL + slot; my_v = val; }
     }
-    const float psum = seg_sum<64>(lane < k ? myp : 0.f);
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    const float myp = lane < k ? expf(my_v - m) : 0.f;
+    const float psum = seg_sum<64>(myp);
     if (lane < k) {
         const float w = myp / psum;
-        o.ids[slot] = myid;
-        o.w[slot] = w;
-        if (o.dbg_ids) o.dbg_ids[slot] = myid;
-        if (o.dbg_w) o.dbg_w[slot] = w;
+        o.ids[lane] = my_id;
+        o.w[lane] = w;
+        if (o.dbg_ids) o.dbg_ids[lane] = my_id;
+        if (o.dbg_w) o.dbg_w[lane] = w;
     }
     if (lane == 0) {
         const float s = sigmoid_f(glog);
@@ -142,18 +106,14 @@ __device__ void route_token(const float *lg, int E, int k, int lane, uint32_t *w
     }
     if (o.dbg_logits)
         for (int e = lane; e < E; e += 64) o.dbg_logits[e] = lg[e];
-    // the wave's LDS is reused by its next token
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ void route_token_any(const float *lg, int E, int k, int lane, uint32_t *wlds,
-                                                const RouteOut &o) {
+__device__ __forceinline__ void route_token_any(const float *lg, int E, int k, int lane, const RouteOut &o) {
     const int epl = (E + 63) / 64;
-    if (epl <= 1) route_token<1>(lg, E, k, lane, wlds, o);
-    else if (epl <= 2) route_token<2>(lg, E, k, lane, wlds, o);
-    else if (epl <= 4) route_token<4>(lg, E, k, lane, wlds, o);
-    else route_token<8>(lg, E, k, lane, wlds, o);
+    if (epl <= 1) route_token<1>(lg, E, k, lane, o);
+    else if (epl <= 2) route_token<2>(lg, E, k, lane, o);
+    else if (epl <= 4) route_token<4>(lg, E, k, lane, o);
+    else route_token<8>(lg, E, k, lane, o);
 }
 
 // LDS ints the bucketing needs for E experts and T tokens.
@@ -286,11 +246,11 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
 // local tables the job records, weights and gates also live in LDS (a
 // workgroup that routes for its own use); without, they only go to memory.
 struct RouteLds {
-    size_t ids, pairs, pose, nu, slots, records, scratch, rank, w, g, bytes;
+    size_t ids, pairs, pose, nu, slots, records, scratch, w, g, bytes;
     bool local;
 };
 
-__host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, int waves, bool local) {
+__host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, bool local) {
     const size_t np = (size_t)T * k, ns = (size_t)(E < T * k ? E : T * k);
     RouteLds L{};
     L.local = local;
@@ -303,7 +263,6 @@ __host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, int wa
     L.slots = o;   o += ns * 16;
     L.scratch = o; o += (size_t)bucket_scratch_ints(E, T) * 4;
     o = (o + 15) & ~(size_t)15;
-    L.rank = o;    o += (size_t)waves * kRankWords * 4;
     if (local) {
         L.records = o; o += ns * kRecInts * 4;
         L.w = o;       o += np * 4;
@@ -334,14 +293,13 @@ __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int 
     int *ids = reinterpret_cast<int *>(area + L.ids);
     float *lw = reinterpret_cast<float *>(area + L.w);
     float *lg = reinterpret_cast<float *>(area + L.g);
-    uint32_t *rank = reinterpret_cast<uint32_t *>(area + L.rank) + wave * kRankWords;
     for (int t = t_lo + wave; t < t_hi; t += nw) {
         RouteOut o{(ids_to_global ? g.ids : ids) + t * k, (g.wts ? g.wts : lw) + t * k,
                    (g.gate_s ? g.gate_s : lg) + t,
                    g.dbg_ids ? g.dbg_ids + t * k : nullptr, g.dbg_w ? g.dbg_w + t * k : nullptr,
                    g.dbg_gate ? g.dbg_gate + t : nullptr,
                    g.dbg_logits ? g.dbg_logits + (size_t)t * E : nullptr};
-        route_token_any(logits + (size_t)t * (E + 1), E, k, lane, rank, o);
+        route_token_any(logits + (size_t)t * (E + 1), E, k, lane, o);
     }
 }
 
