@@ -282,6 +282,19 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
         loaded = true;
     }
+    // tokens to stage: with in-kernel routing their loads go out before it, so that
+    // they arrive while the batch is ranked (up to 4 chunks per thread)
+    constexpr int kXPre = 4;
+    const int n16 = p.x_resident ? (int)(T * xrow / 16) : 0;
+    const bool x_early = route_here && n16 <= kXPre * 256;
+    uint4 xpre[kXPre];
+    if (x_early) {
+#pragma unroll
+        for (int q = 0; q < kXPre; ++q) {
+            const int i = tid + 256 * q;
+            if (i < n16) xpre[q] = ld16((const uint8_t *)p.x + 16 * (size_t)i);
+        }
+    }
     if (route_here) {
         // every workgroup ranks and buckets the whole batch; workgroup 0 publishes
         uint8_t *area = lds + p.route_lds_off;
@@ -304,8 +317,14 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
     }
     // tokens staged once, their loads in flight together with the first job's weights
-    if (p.x_resident) {
-        const int n16 = (int)(T * xrow / 16);
+    if (x_early) {
+#pragma unroll
+        for (int q = 0; q < kXPre; ++q) {
+            const int i = tid + 256 * q;
+            if (i < n16) reinterpret_cast<uint4 *>(lds)[i] = xpre[q];
+        }
+        __syncthreads();
+    } else if (p.x_resident) {
         for (int i = tid; i < n16; i += 256)
             reinterpret_cast<uint4 *>(lds)[i] = ld16((const uint8_t *)p.x + 16 * (size_t)i);
         __syncthreads();

@@ -303,7 +303,8 @@ __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int 
     }
 }
 
-// With every id in LDS: buckets the pairs and builds the job records in LDS;
+// With every id in LDS: buckets the pairs and builds the job records in LDS
+// (expert-ascending buckets; a single token's buckets follow its rank order);
 // copies the tables to g where its pointers are set.  Barriers inside: call
 // from every thread of the workgroup.  Returns the used-expert count.
 __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const RouteLds &L,
@@ -316,7 +317,18 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
     int4 *slots = reinterpret_cast<int4 *>(area + L.slots);
     int *rec = reinterpret_cast<int *>(area + L.records);
     __syncthreads();
-    if (NP <= 16) {  // measured: one wave wins up to 16 pairs, the whole workgroup above
+    if (T == 1) {  // one token: its k picks are k distinct experts, one bucket each, in rank order
+        if (threadIdx.x < 64) {
+            const int j = threadIdx.x;
+            if (j < k) {
+                const int e = ids[j];
+                slots[j] = make_int4(e, j, 1, 0);
+                pairs[j] = j;
+                pose[j] = e;
+            }
+            if (j == 0) *nup = k;
+        }
+    } else if (NP <= 16) {  // measured: one wave wins up to 16 pairs, the whole workgroup above
         if (threadIdx.x < 64) bucket_pairs_wave(ids, NP, E, slots, pairs, pose, nup);
     } else {
         bucket_pairs(ids, T, k, E, reinterpret_cast<uint32_t *>(area + L.scratch), slots, pairs, pose, nup);
