@@ -125,7 +125,7 @@ typedef enum moe_ffn_dtype {
 /* Shapes and storage; frozen for the life of the plan.
  * Limits (else MOE_FFN_ERR_UNSUPPORTED): hidden, inter, shared_inter
  * multiples of 32 and at most 8192; n_experts 1..512; top_k 1..32 and
- * <= n_experts; max_tokens 1..256; supported storage pairs (x_dtype,
+ * <= n_experts; max_tokens 1..16384; supported storage pairs (x_dtype,
  * weight_dtype): (F32, F32), (BF16, BF16), (BF16, Q4_B32). */
 typedef struct moe_ffn_desc {
     int32_t hidden;             /* H */
@@ -189,11 +189,12 @@ typedef struct moe_ffn_plan_info {
 
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
-    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit); for batches above
-                                   32 tokens also the routing, in the same launch */
+    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit); for batches of
+                                   33..256 tokens also the routing, in the same launch */
     MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) up to 32 tokens,
                                    except up to 4 tokens in the mat-vec regime, where the routed
-                                   gate/up launch routes */
+                                   gate/up launch routes; above 256 tokens the ranking launch
+                                   (top-k, renormalisation, per-expert counts) */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
     MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */
@@ -202,7 +203,8 @@ typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up (routed, or routed + shared when fused) */
     MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN_JOIN = 9,    /* mat-vec regime: down of every pair of a row tile + the join */
-    MOE_FFN_K_COUNT = 10
+    MOE_FFN_K_BUCKET = 10,      /* above 256 tokens: bucketing of the ranked pairs by expert */
+    MOE_FFN_K_COUNT = 11
 } moe_ffn_kernel_id;
 
 int32_t moe_ffn_abi_version(void);

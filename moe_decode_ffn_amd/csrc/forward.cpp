@@ -264,7 +264,10 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     // else a routing launch of its own (one wave per token) or the router's tail
     const bool route_kernel = !gp.route_here && Ti <= kRouteKernelMax &&
                               route_kernel_lds_bytes(Ti, (int)k, (int)E) <= kLdsLimit;
-    rp.route_tail = gp.route_here || route_kernel ? 0 : 1;
+    // large batches: ranking and bucketing launches of their own, through global memory
+    const bool batch_route = Ti > kTailMaxTokens;
+    rp.route_tail = gp.route_here || route_kernel || batch_route ? 0 : 1;
+    rp.bcount = batch_route ? (int *)(W + L.bcount) : nullptr;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
     gp.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
     const int gu_tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
@@ -286,8 +289,11 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gg.Is = (int)Is; gg.records = records; gg.n_unique = n_unique; gg.pairs = pairs;
     gg.hb = (uint16_t *)h; gg.shb = (uint16_t *)sh_h; gg.y = y; gg.S = sh_S;
     const int gg_rows = gg_rows_per_job();
-    // 16 tokens per MFMA pass; the shared expert's tokens are split into blocks of 16
-    const int gg_nt = 1;
+    // 16 tokens per MFMA tile; a pass takes 1, 2 or 4 tiles by the mean bucket size (more
+    // tokens per pass read each expert's weights fewer times); the shared expert's tokens
+    // are split into blocks of one pass
+    const size_t mean_bucket = T * k / std::max<size_t>(1, std::min(E, T * k));
+    const int gg_nt = mean_bucket >= 48 ? 4 : mean_bucket >= 24 ? 2 : 1;
     const int gg_tb = (Ti + 16 * gg_nt - 1) / (16 * gg_nt);
     auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
 
@@ -314,8 +320,12 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     auto run_router = [&](hipStream_t s) {
         hipError_t e1 = timed(P, MOE_FFN_K_ROUTER, s,
                               [&] { return launch_router(rp, P->map_router, r_grid, r_tiles, s); });
-        if (e1 != hipSuccess || !route_kernel) return e1;
-        return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(rp, s); });
+        if (e1 != hipSuccess) return e1;
+        if (route_kernel) return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(rp, s); });
+        if (!batch_route) return e1;
+        e1 = timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_rank_batch(rp, s); });
+        if (e1 != hipSuccess) return e1;
+        return timed(P, MOE_FFN_K_BUCKET, s, [&] { return launch_bucket_batch(rp, s); });
     };
     // grid of a grid-stride expert launch: its jobs, capped at the resident workgroups
     auto expert_grid = [&](int jobs, int occ) { return std::max(1, std::min(jobs, occ * P->cu_count)); };

@@ -14,15 +14,16 @@
 
 namespace moeffn {
 
-constexpr int kMaxTokens = 256;
+constexpr int kMaxTokens = 16384;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
 constexpr int kDefaultMatvecMax = 6;  // measured crossover of the mat-vec and grouped-GEMM kernels
 constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
 constexpr int kRouteKernelMax = 32;   // up to this batch k_route routes it (else the router tail)
+constexpr int kTailMaxTokens = 256;   // up to this batch the router tail routes it (else batch routing)
 // arrival counters in plan memory: one per router token tile, one across tiles
-constexpr int kTicketCount = kMaxTokens + 1;
+constexpr int kTicketCount = kTailMaxTokens + 1;
 constexpr size_t kWsAlign = 256;
 constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
 constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
@@ -54,6 +55,7 @@ struct Layout {
     size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
     size_t logits = 0;     // f32 [Tmax][E+1] (column E = shared-gate logit), router -> gate/up
     size_t xn = 0;         // x_dtype [Tmax][H]: normalised input (INPUT_NORM), router -> experts
+    size_t bcount = 0;     // i32 [4][E]: batch routing's per-expert count, cursor, offset, slot
     size_t routing_bytes = 0;
     // phase region: reused by the sequential steps
     size_t h = 0;       // gate/up -> down: f32 [Tmax*k][I]
@@ -120,12 +122,15 @@ struct RouterParams {
     int *pos_expert;        // [T*k]
     int32_t *dbg_ids;
     float *dbg_w, *dbg_logits, *dbg_gate;
-    unsigned *tickets;      // plan memory: [kMaxTokens] per token tile + [1] across tiles, zero between calls
+    unsigned *tickets;      // plan memory: [kTailMaxTokens] per token tile + [1] across tiles, zero between calls
     int route_tail;         // 1: the launch also ranks and buckets (else k_route or the gate/up launch)
     // input RMSNorm: logits from the normalised tokens; workgroup column 0 writes them for the experts
     const float *norm_w;    // [H] or NULL: no norm
     float norm_eps;
     void *xn;               // [T][H] x_dtype
+    // batch routing (large batches): workgroup (0, 0) zeroes the per-expert counts and
+    // cursors; k_rank_batch ranks and counts, k_bucket_batch scans and scatters
+    int *bcount;            // [4][E] or NULL
 };
 
 struct GateUpParams {
@@ -274,6 +279,8 @@ size_t router_lds_bytes(const RouterParams &p);
 size_t route_lds_bytes(int T, int k, int E);
 size_t route_kernel_lds_bytes(int T, int k, int E);
 hipError_t launch_route(const RouterParams &p, hipStream_t s);
+hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s);
+hipError_t launch_bucket_batch(const RouterParams &p, hipStream_t s);
 int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds);
 
 // ---- planner helpers (plan.cpp) ---------------------------------------------

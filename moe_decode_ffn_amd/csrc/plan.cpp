@@ -106,7 +106,7 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
             return set_error(MOE_FFN_ERR_UNSUPPORTED, "hidden/inter/shared_inter must be multiples of 32, at most 8192");
     if (d.n_experts > kMaxExperts) return set_error(MOE_FFN_ERR_UNSUPPORTED, "n_experts > 512");
     if (d.top_k > kMaxTopK) return set_error(MOE_FFN_ERR_UNSUPPORTED, "top_k > 32");
-    if (d.max_tokens > kMaxTokens) return set_error(MOE_FFN_ERR_UNSUPPORTED, "max_tokens > 256");
+    if (d.max_tokens > kMaxTokens) return set_error(MOE_FFN_ERR_UNSUPPORTED, "max_tokens > 16384");
     const bool pair_ok = (d.x_dtype == MOE_FFN_F32 && d.weight_dtype == MOE_FFN_F32) ||
                          (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_BF16) ||
                          (d.x_dtype == MOE_FFN_BF16 && d.weight_dtype == MOE_FFN_Q4_B32);
@@ -143,7 +143,9 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     rq.H = H; rq.x_bf16 = xbytes == 2;
     rq.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
     const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
-    if (!maps_ok || router_lds_bytes(rq) > kLdsLimit || route_lds_bytes(d.max_tokens, k, E) > kLdsLimit) {
+    // LDS routing runs up to kTailMaxTokens tokens; larger batches route through global memory
+    if (!maps_ok || router_lds_bytes(rq) > kLdsLimit ||
+        route_lds_bytes(std::min(d.max_tokens, kTailMaxTokens), k, E) > kLdsLimit) {
         delete P;
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
     }
@@ -163,6 +165,8 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.logits = c;     c += align_up(T * (E + 1) * 4);
     // normalised input of both branches (x_dtype), router -> experts
     L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
+    // per-expert count, cursor, offset and slot of batch routing (batches above kTailMaxTokens)
+    L.bcount = c;     c += d.max_tokens > kTailMaxTokens ? align_up((size_t)4 * E * 4) : 0;
     L.routing_bytes = c - L.shared_bytes;
     // sequential steps: gate/up holds h, down holds h and y, join holds y
     const size_t base = c;

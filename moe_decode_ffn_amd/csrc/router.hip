@@ -85,6 +85,9 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
                                        : make_float4(1.f, 1.f, 1.f, 1.f);
     }
 
+    if (p.bcount && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = tid; i < 2 * E; i += 256) p.bcount[i] = 0;  // counts and cursors
+
     const int t0 = blockIdx.y * p.tok_tile;
     const int nt = min(p.tok_tile, p.T - t0);
     // the normalised tokens of the tile are written by the column's workgroups in
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
                         p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
     rank_tokens(p.logits, t0, t0 + nt, E, k, lds, L, g, !one_tile);
     if (!one_tile) {
-        if (!last_arrival(p.tickets + kMaxTokens, gridDim.y)) return;
+        if (!last_arrival(p.tickets + kTailMaxTokens, gridDim.y)) return;
         int *ids = reinterpret_cast<int *>(lds + L.ids);
         for (int i = tid; i < T * k; i += blockDim.x) ids[i] = p.ids[i];
     }
@@ -207,6 +210,97 @@ __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
                         p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
     rank_tokens(p.logits, 0, p.T, p.E, p.k, lds, L, g, false);
     bucket_tokens(p.T, p.k, p.E, lds, L, g);
+}
+
+// ---- batch routing (large batches) ----------------------------------------------------
+// k_rank_batch: each wave ranks kRankTokensPerWave tokens in turn and counts its picks
+// per expert (integer atomics: the counts are exact whatever the order).
+constexpr int kRankTokensPerWave = 4;
+constexpr int kRankTokensPerWg = 4 * kRankTokensPerWave;
+
+__global__ __launch_bounds__(256) void k_rank_batch(RouterParams p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = p.E, k = p.k;
+    int *cnt = p.bcount;
+    for (int i = 0; i < kRankTokensPerWave; ++i) {
+        const int t = blockIdx.x * kRankTokensPerWg + i * 4 + wave;
+        if (t >= p.T) break;
+        RouteOut o{p.ids + (size_t)t * k, p.wts + (size_t)t * k, p.gate_s + t,
+                   p.dbg_ids ? p.dbg_ids + (size_t)t * k : nullptr, p.dbg_w ? p.dbg_w + (size_t)t * k : nullptr,
+                   p.dbg_gate ? p.dbg_gate + t : nullptr, p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
+        route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
+        if (lane < k) {
+            const int e = o.ids[lane];  // this lane's own store: visible to it
+            if (e >= 0 && e < E) atomicAdd(cnt + e, 1);
+        }
+    }
+}
+
+// k_bucket_batch: every workgroup scans the counts (expert offsets, used-expert
+// slots) in LDS; workgroup 0 writes the job records and the used-expert count;
+// every workgroup places its pairs, each at its expert's offset plus a cursor
+// taken atomically.  Within an expert the order of the pairs depends on timing,
+// but no result does: every pair's rows are computed alone and the join sums a
+// token's slots in slot order.
+constexpr int kBucketPairsPerWg = 1024;
+
+__global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
+    __shared__ int s_off[kMaxExperts], s_slot[kMaxExperts], s_wsum[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = p.E, NP = p.T * p.k;
+    const int *cnt = p.bcount;
+    int *cur = p.bcount + E;
+    // exclusive scans of cnt[] and (cnt[] > 0): thread owns two consecutive experts
+    const int e0 = 2 * tid;
+    const int c0 = e0 < E ? cnt[e0] : 0, c1 = e0 + 1 < E ? cnt[e0 + 1] : 0;
+    int a = c0 + c1, b = (c0 > 0) + (c1 > 0);
+    int ia = a, ib = b;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int ya = __shfl_up(ia, d), yb = __shfl_up(ib, d);
+        if (lane >= d) { ia += ya; ib += yb; }
+    }
+    if (lane == 63) { s_wsum[0][wave] = ia; s_wsum[1][wave] = ib; }
+    __syncthreads();
+    int ba = ia - a, bb = ib - b;
+    for (int w = 0; w < wave; ++w) { ba += s_wsum[0][w]; bb += s_wsum[1][w]; }
+    if (e0 < E) { s_off[e0] = ba; s_slot[e0] = c0 > 0 ? bb : -1; }
+    if (e0 + 1 < E) { s_off[e0 + 1] = ba + c0; s_slot[e0 + 1] = c1 > 0 ? bb + (c0 > 0) : -1; }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < E; e += 256) {
+            const int u = s_slot[e];
+            if (u < 0) continue;
+            const int c = cnt[e];
+            int *rec = p.records + (size_t)u * kRecInts;
+            rec[0] = e; rec[1] = s_off[e]; rec[2] = c; rec[3] = 0;
+            for (int f = c; f < kRecPairs; ++f) rec[4 + f] = -1;  // the pairs themselves come below
+        }
+        if (tid == 0) *p.n_unique = s_wsum[1][0] + s_wsum[1][1] + s_wsum[1][2] + s_wsum[1][3];
+    }
+    const int q_end = min(NP, (blockIdx.x + 1) * kBucketPairsPerWg);
+    for (int q = blockIdx.x * kBucketPairsPerWg + tid; q < q_end; q += 256) {
+        const int e = p.ids[q];
+        if (e < 0 || e >= E) continue;
+        const int r = atomicAdd(cur + e, 1);
+        const int pos = s_off[e] + r;
+        if (r >= cnt[e] || pos >= NP) continue;  // only with a corrupt count
+        p.pairs[pos] = q;
+        p.pos_expert[pos] = e;
+        if (r < kRecPairs) p.records[(size_t)s_slot[e] * kRecInts + 4 + r] = q;
+    }
+}
+
+hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s) {
+    const int grid = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    launch_kernel(k_rank_batch, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bucket_batch(const RouterParams &p, hipStream_t s) {
+    if (p.E > 2 * 256) return hipErrorInvalidValue;
+    const int grid = (p.T * p.k + kBucketPairsPerWg - 1) / kBucketPairsPerWg;
+    launch_kernel(k_bucket_batch, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 int route_kernel_waves(int T) { return T < 4 ? 4 : T > 16 ? 16 : T; }

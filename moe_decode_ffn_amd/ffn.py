@@ -28,7 +28,7 @@ INPUT_NORM, RESIDUAL = 0x1000, 0x2000
 DEBUG_DELAY_AUX, DEBUG_DELAY_MAIN, DEBUG_SPLIT_JOIN = 0x100, 0x200, 0x400
 # moe_ffn_kernel_id
 KERNELS = ("router", "route", "gate_up", "down", "sh_gate_up", "sh_down", "join", "gg_gate_up",
-           "gg_down", "down_join")
+           "gg_down", "down_join", "bucket")
 K_COUNT = len(KERNELS)
 
 DTYPES = {"f32": F32, "bf16": BF16, "q4": Q4_B32}

@@ -78,6 +78,8 @@ WORKLOADS = {
     "decode_bf16_t8": (DECODE_BF16, 2, (8,)),
     "decode_q4_t1_t4": (DECODE_Q4, 3, (1, 4)),
     "decode_bf16_t128": (DECODE_BF16, 4, (128,)),
+    # a prefill chunk: every expert busy, ~128 tokens per expert
+    "prefill_bf16_t4096": (DECODE_BF16, 5, (4096,)),
 }
 
 

@@ -88,7 +88,7 @@ BAD_PLANS = [
     (dict(hidden=16384), ffn.ERR_UNSUPPORTED),
     (dict(n_experts=1024, top_k=8), ffn.ERR_UNSUPPORTED),
     (dict(top_k=33, n_experts=64), ffn.ERR_UNSUPPORTED),
-    (dict(max_tokens=257), ffn.ERR_UNSUPPORTED),
+    (dict(max_tokens=16385), ffn.ERR_UNSUPPORTED),
     (dict(x_dtype=ffn.F32, weight_dtype=ffn.BF16), ffn.ERR_UNSUPPORTED),
     (dict(x_dtype=ffn.BF16, weight_dtype=ffn.F32), ffn.ERR_UNSUPPORTED),
     # the grouped GEMM takes bf16 storage with sizes that are multiples of 128
@@ -166,6 +166,21 @@ def test_plan_rejects_bad_norm_eps(lib, eps):
     assert e.value.status == ffn.ERR_INVALID_ARG
     p, _ = ffn.moe_ffn_plan(desc(flags=ffn.INPUT_NORM, norm_eps=0.0))  # eps 0 is allowed
     ffn.moe_ffn_destroy(p)
+
+
+@pytest.mark.parametrize("T", [257, 4096])
+def test_workspace_with_batch_routing(lib, T):
+    # above 256 tokens the routing region also holds four per-expert int arrays
+    # (count, cursor, offset, slot) for the ranking and bucketing launches
+    H, E, k, I, Is = 2048, 256, 8, 512, 512
+    plan, ws = ffn.moe_ffn_plan(desc(max_tokens=T))
+    info = ffn.moe_ffn_plan_get_info(plan)
+    ffn.moe_ffn_destroy(plan)
+    routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(4 * E * 4))
+    assert info.routing_region_bytes == routing
+    assert ws == info.workspace_bytes == (_align(T * Is * 4) + _align(T * H * 4) + routing
+                                          + _align(T * k * I * 4) + _align(T * k * H * 4))
 
 
 def test_auto_mode_defaults(lib):

@@ -1,0 +1,139 @@
+"""GPU parity of large batches (prefill): above 256 tokens the batch is ranked by
+its own launch (one wave per token, per-expert counts) and bucketed by another
+(offsets from the counts, positions from atomic cursors), through global memory.
+
+The order of pairs inside an expert's bucket then depends on timing, so these
+tests also check that no output does: repeated runs must agree bit for bit.
+Small layers are checked against the oracle on every token; the decode layer
+at full size on a sample of tokens (each token's output depends on that token
+alone, so the oracle runs on the sample).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from moe_decode_ffn_amd import ffn, synth
+from tests.gpu_common import compare, device, oracle_threads, run_gpu, tol_for
+from tests.helpers import oracle_layer, oracle_tokens
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"aux": ffn.SHARED_AUX, "seq": ffn.SHARED_SEQ, "fused": ffn.SHARED_FUSED}
+
+SMALL = {
+    # name: (shape, seed, token counts, regime flags)
+    "bf16_gemm": (synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16"), 40, (257, 300, 777), 0),
+    "bf16_matvec": (synth.LayerShape(160, 12, 3, 96, 64, "bf16", "bf16"), 41, (300, 520), 0),
+    "q4": (synth.LayerShape(192, 10, 3, 96, 160, "bf16", "q4"), 42, (400,), 0),
+    "fp32": (synth.LayerShape(288, 20, 4, 64, 96, "f32", "f32"), 43, (300,), 0),
+    # 16384 pairs over 64 experts: buckets of ~256 tokens, 64-token GEMM passes
+    "bf16_big_buckets": (synth.LayerShape(128, 64, 16, 128, 128, "bf16", "bf16"), 44, (1024,), 0),
+    "bf16_gemm_matvec_forced": (synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16"), 45, (300,),
+                                ffn.FORCE_MATVEC),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layers_all_modes(orc, name):
+    dev = device()
+    shape, seed, counts, regime = SMALL[name]
+    layer = synth.make_layer(shape, seed)
+    dl = synth.layer_to(layer, dev)
+    plans = {m: ffn.MoeFfn.for_shape(shape, max_tokens=max(counts), flags=f | regime) for m, f in MODES.items()}
+    for T in counts:
+        x = synth.make_tokens(shape, T, seed, stream=T)
+        ref = orc.forward(oracle_layer(layer), oracle_tokens(x), nthreads=oracle_threads())
+        outs = {}
+        for m, mf in plans.items():
+            print(f"[prefill] {name} T={T} mode={m}", flush=True)
+            got = run_gpu(mf, dl, x.to(dev))
+            rep = compare(orc, layer, x, got, tol_for(shape), ref=ref)
+            outs[m] = got["out"]
+        print(f"  {rep}", flush=True)
+        assert torch.equal(outs["aux"], outs["seq"]), "aux vs sequential must be bit-identical"
+        assert torch.equal(outs["aux"], outs["fused"]), "aux vs fused must be bit-identical"
+    for mf in plans.values():
+        mf.close()
+
+
+def test_input_block_large_batch(orc):
+    dev = device()
+    shape = synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16")
+    layer = synth.with_input_block(synth.make_layer(shape, 46), 346)
+    dl = synth.layer_to(layer, dev)
+    x = synth.make_tokens(shape, 600, 46)
+    ref = orc.forward(oracle_layer(layer), oracle_tokens(x), nthreads=oracle_threads())
+    outs = {}
+    for m, f in MODES.items():
+        print(f"[prefill] input block T=600 mode={m}", flush=True)
+        mf = ffn.MoeFfn.for_layer(layer, 600, flags=f)
+        got = run_gpu(mf, dl, x.to(dev))
+        compare(orc, layer, x, got, tol_for(shape), ref=ref)
+        outs[m] = got["out"]
+        mf.close()
+    assert torch.equal(outs["aux"], outs["seq"]) and torch.equal(outs["aux"], outs["fused"])
+
+
+def test_max_tokens_16384(orc):
+    dev = device()
+    shape = synth.LayerShape(128, 16, 2, 128, 128, "bf16", "bf16")
+    layer = synth.make_layer(shape, 47)
+    x = synth.make_tokens(shape, 16384, 47)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=16384)
+    print("[prefill] 16384 tokens", flush=True)
+    got = run_gpu(mf, synth.layer_to(layer, dev), x.to(dev))
+    compare(orc, layer, x, got, tol_for(shape))
+    mf.close()
+
+
+def _subset(got: dict, idx: np.ndarray) -> dict:
+    return {k: v[torch.from_numpy(idx)] for k, v in got.items()}
+
+
+FULL = {
+    # name: (shape, seed, tokens, sampled tokens checked against the oracle)
+    "decode_bf16_t2048": (synth.DECODE_BF16, 5, 2048, 48),
+    "decode_q4_t512": (synth.DECODE_Q4, 6, 512, 32),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(orc, name):
+    """All modes bit-identical on every token; a sample of tokens against the oracle."""
+    dev = device()
+    shape, seed, T, n_check = FULL[name]
+    dl = synth.make_layer_device(shape, seed, dev)
+    lc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dl.items()}
+    x = synth.make_tokens(shape, T, seed, stream=T)
+    idx = np.sort(np.random.default_rng(seed).choice(T, n_check, replace=False))
+    ref = orc.forward(oracle_layer(lc), oracle_tokens(x[torch.from_numpy(idx)]), nthreads=oracle_threads())
+    outs = {}
+    for m, f in MODES.items():
+        print(f"[prefill] {name} mode={m}", flush=True)
+        mf = ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=f)
+        got = run_gpu(mf, dl, x.to(dev))
+        rep = compare(orc, lc, x[torch.from_numpy(idx)], _subset(got, idx), tol_for(shape), ref=ref)
+        print(f"  {rep}", flush=True)
+        outs[m] = got["out"]
+        assert torch.all(torch.isfinite(got["out"]))
+        mf.close()
+    assert torch.equal(outs["aux"], outs["seq"])
+    assert torch.equal(outs["aux"], outs["fused"])
+
+
+def test_bucket_order_does_not_change_results():
+    """Batch routing places pairs by atomic cursors; repeated runs (with the
+    workspace poisoned in between) must still give the same bits."""
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 5, 2048
+    dl = synth.make_layer_device(shape, seed, dev)
+    x = synth.make_tokens(shape, T, seed, stream=7).to(dev)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
+    ws = torch.empty(mf.workspace_bytes, dtype=torch.uint8, device=dev)
+    first = run_gpu(mf, dl, x, ws=ws, poison=0)["out"]
+    for i, pat in enumerate((0xFF, 0xA5, 0x00, 0x7F)):
+        print(f"[prefill] repeat {i}", flush=True)
+        assert torch.equal(run_gpu(mf, dl, x, ws=ws, poison=pat)["out"], first), f"run {i}"
+    mf.close()
