@@ -103,11 +103,16 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
     P->occ_d = expert_kernel_occupancy(false, P->wkind, P->map_down, 0);
-    if (P->gemm_ok)
+    if (P->gemm_ok) {
         for (int i = 0; i < 3; ++i) {
             P->occ_gg_gu[i] = gg_occupancy(true, 1 << i);
             P->occ_gg_d[i] = gg_occupancy(false, 1 << i);
         }
+        for (int i = 0; i < 2; ++i) {
+            P->occ_pf_gu[i] = pf_occupancy(true, 2 << i);
+            P->occ_pf_d[i] = pf_occupancy(false, 2 << i);
+        }
+    }
     P->ready = true;
     return MOE_FFN_OK;
 }
@@ -294,6 +299,10 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     // are split into blocks of one pass
     const size_t mean_bucket = T * k / std::max<size_t>(1, std::min(E, T * k));
     const int gg_nt = mean_bucket >= 48 ? 4 : mean_bucket >= 24 ? 2 : 1;
+    // large buckets: the prefill GEMM (weight stages shared through LDS, 128 or 256 tokens
+    // per pass)
+    const bool pf = gemm && mean_bucket >= (size_t)kPfMinBucket;
+    const int pf_ntw = mean_bucket >= 160 ? 4 : 2;
     const int gg_tb = (Ti + 16 * gg_nt - 1) / (16 * gg_nt);
     auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
 
@@ -349,7 +358,27 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
             return launch_down(q, wk, P->map_down, expert_grid(jobs, P->occ_d), s);
         });
     };
+    auto run_pf = [&](hipStream_t s, bool gate_up, bool routed, bool shared) {
+        GGParams g = gg;
+        if (gate_up) {
+            g.w0 = (const uint8_t *)t->w_gate; g.w1 = (const uint8_t *)t->w_up;
+            g.sw0 = (const uint8_t *)t->sh_gate; g.sw1 = (const uint8_t *)t->sh_up;
+        } else {
+            g.w0 = (const uint8_t *)t->w_down; g.sw0 = (const uint8_t *)t->sh_down;
+        }
+        const int rows = pf_rows_per_job(gate_up);
+        g.routed = routed ? 1 : 0;
+        g.tiles_routed = (int)(((gate_up ? I : H) + rows - 1) / rows);
+        g.tiles_shared = shared ? (int)(((gate_up ? Is : H) + rows - 1) / rows) : 0;
+        const int bn = pf_tokens_per_pass(pf_ntw);
+        const int jobs = g.tiles_shared * ((Ti + bn - 1) / bn) + (routed ? max_used * g.tiles_routed : 0);
+        const int occ = (gate_up ? P->occ_pf_gu : P->occ_pf_d)[pf_ntw >= 4 ? 1 : 0];
+        const int kid = routed ? (gate_up ? MOE_FFN_K_GG_GATE_UP : MOE_FFN_K_GG_DOWN)
+                               : (gate_up ? MOE_FFN_K_SH_GATE_UP : MOE_FFN_K_SH_DOWN);
+        return timed(P, kid, s, [&] { return launch_pf(g, gate_up, pf_ntw, expert_grid(jobs, occ), s); });
+    };
     auto run_gg_gate_up = [&](hipStream_t s, bool routed, bool shared) {
+        if (pf) return run_pf(s, true, routed, shared);
         GGParams g = gg;
         g.w0 = (const uint8_t *)t->w_gate; g.w1 = (const uint8_t *)t->w_up;
         g.sw0 = (const uint8_t *)t->sh_gate; g.sw1 = (const uint8_t *)t->sh_up;
@@ -364,6 +393,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         });
     };
     auto run_gg_down = [&](hipStream_t s, bool routed, bool shared) {
+        if (pf) return run_pf(s, false, routed, shared);
         GGParams g = gg;
         g.w0 = (const uint8_t *)t->w_down; g.sw0 = (const uint8_t *)t->sh_down;
         g.routed = routed ? 1 : 0;

@@ -22,6 +22,7 @@ constexpr int kDefaultMatvecMax = 6;  // measured crossover of the mat-vec and g
 constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
 constexpr int kRouteKernelMax = 32;   // up to this batch k_route routes it (else the router tail)
 constexpr int kTailMaxTokens = 256;   // up to this batch the router tail routes it (else batch routing)
+constexpr int kPfMinBucket = 32;      // mean tokens per used expert from which the prefill GEMM runs
 // arrival counters in plan memory: one per router token tile, one across tiles
 constexpr int kTicketCount = kTailMaxTokens + 1;
 constexpr size_t kWsAlign = 256;
@@ -88,6 +89,7 @@ struct moe_ffn_plan_s {
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
+    int occ_pf_gu[2] = {0, 0}, occ_pf_d[2] = {0, 0};        // prefill GEMM, 128/256 tokens per pass
     bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
     // profiling
     bool profiling = false;
@@ -280,6 +282,12 @@ size_t route_lds_bytes(int T, int k, int E);
 size_t route_kernel_lds_bytes(int T, int k, int E);
 hipError_t launch_route(const RouterParams &p, hipStream_t s);
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s);
+// prefill grouped GEMM (large buckets)
+size_t pf_lds_bytes();
+int pf_rows_per_job(bool gate_up);
+int pf_tokens_per_pass(int ntw);
+hipError_t launch_pf(const GGParams &p, bool gate_up, int ntw, int grid, hipStream_t s);
+int pf_occupancy(bool gate_up, int ntw);
 hipError_t launch_bucket_batch(const RouterParams &p, hipStream_t s);
 int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds);
 
