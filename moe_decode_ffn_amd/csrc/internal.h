@@ -282,6 +282,7 @@ size_t route_lds_bytes(int T, int k, int E);
 size_t route_kernel_lds_bytes(int T, int k, int E);
 hipError_t launch_route(const RouterParams &p, hipStream_t s);
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s);
+hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s);
 // prefill grouped GEMM (large buckets)
 size_t pf_lds_bytes();
 int pf_rows_per_job(bool gate_up);

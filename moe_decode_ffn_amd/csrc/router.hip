@@ -212,6 +212,118 @@ __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
     bucket_tokens(p.T, p.k, p.E, lds, L, g);
 }
 
+// ---- router GEMM for large batches ------------------------------------------------------
+// logits[t][e] = sum_h W[e][h] x[t][h] on v_mfma_f32_16x16x32_bf16.  The tokens are bf16;
+// each fp32 router weight is split exactly into three bf16 pieces (hi = the top 16 bits,
+// mid = the top 16 bits of the rest, lo = what remains, at most 8 significant bits), so
+// every product piece * token is exact in fp32 and the three accumulate into one fp32
+// sum: the logits carry fp32-GEMV accuracy.  A wave owns 16 rows (experts, the gate
+// vector as row E) and 64 tokens; a workgroup 64 rows.  K in steps of 32; lane group g
+// holds elements 8g..8g+7 of a step for both operands.
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rfloatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rfloatx4_t r_mfma(uint4 a, uint4 b, rfloatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rbf16x8_t, a),
+                                                   __builtin_bit_cast(rbf16x8_t, b), c, 0, 0, 0);
+}
+
+// eight fp32 -> three bf16x8 planes whose sum is exact
+__device__ __forceinline__ void split3(const float4 &u, const float4 &v, uint4 &hi, uint4 &mid, uint4 &lo) {
+    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t b = __float_as_uint(f[i]);
+        const float fh = __uint_as_float(b & 0xffff0000u);
+        const float r1 = f[i] - fh;
+        const uint32_t bm = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(bm);
+        h[i] = b >> 16;
+        m[i] = bm >> 16;
+        l[i] = __float_as_uint(r2) >> 16;
+    }
+    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    mid = make_uint4(m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16));
+    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+constexpr int kRgRows = 64;    // rows per workgroup (16 per wave)
+constexpr int kRgTokens = 64;  // tokens per workgroup (four 16-token tiles per wave)
+
+__global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ri = lane & 15, g = lane >> 4;
+    const int H = p.H, E = p.E, T = p.T;
+    if (p.bcount && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = tid; i < 2 * E; i += 256) p.bcount[i] = 0;  // counts and cursors
+    const int row = blockIdx.x * kRgRows + wave * 16 + ri;      // A row of this lane
+    const bool rok = row <= E;
+    const float *W = row < E ? p.router + (size_t)row * H : p.gate_vec;
+    const int t0 = blockIdx.y * kRgTokens;
+    const uint16_t *xb[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int t = t0 + 16 * n + ri;
+        tok_ok[n] = t < T;
+        xb[n] = reinterpret_cast<const uint16_t *>(p.x) + (size_t)(tok_ok[n] ? t : 0) * H;
+    }
+    rfloatx4_t acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[n] = rfloatx4_t{0.f, 0.f, 0.f, 0.f};
+    float4 wa, wb, nwa, nwb;
+    uint4 b[4], nb[4];
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    wa = rok ? *reinterpret_cast<const float4 *>(W + 8 * g) : z4;
+    wb = rok ? *reinterpret_cast<const float4 *>(W + 8 * g + 4) : z4;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) b[n] = tok_ok[n] ? ld16(xb[n] + 8 * g) : make_uint4(0, 0, 0, 0);
+    const int nstep = H / 32;
+    for (int s = 0; s < nstep; ++s) {
+        const bool more = s + 1 < nstep;
+        if (more) {
+            const int ko = 32 * (s + 1) + 8 * g;
+            nwa = rok ? *reinterpret_cast<const float4 *>(W + ko) : z4;
+            nwb = rok ? *reinterpret_cast<const float4 *>(W + ko + 4) : z4;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) nb[n] = tok_ok[n] ? ld16(xb[n] + ko) : make_uint4(0, 0, 0, 0);
+        }
+        uint4 hi, mid, lo;
+        split3(wa, wb, hi, mid, lo);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            acc[n] = r_mfma(hi, b[n], acc[n]);
+            acc[n] = r_mfma(mid, b[n], acc[n]);
+            acc[n] = r_mfma(lo, b[n], acc[n]);
+        }
+        if (more) {
+            wa = nwa;
+            wb = nwb;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) b[n] = nb[n];
+        }
+    }
+    // lane holds rows 4g + v of the wave's 16 for token column ri
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int t = t0 + 16 * n + ri;
+        if (t >= T) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int e = blockIdx.x * kRgRows + wave * 16 + 4 * g + v;
+            if (e <= E) p.logits[(size_t)t * (E + 1) + e] = acc[n][v];
+        }
+    }
+}
+
+hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s) {
+    if (!p.x_bf16 || p.norm_w || p.H % 32 != 0) return hipErrorInvalidValue;
+    const dim3 grid((p.E + 1 + kRgRows - 1) / kRgRows, (p.T + kRgTokens - 1) / kRgTokens);
+    launch_kernel(k_router_mfma, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 // ---- batch routing (large batches) ----------------------------------------------------
 // k_rank_batch: each wave ranks kRankTokensPerWave tokens in turn and counts its picks
 // per expert (integer atomics: the counts are exact whatever the order).

@@ -137,3 +137,23 @@ def test_bucket_order_does_not_change_results():
         print(f"[prefill] repeat {i}", flush=True)
         assert torch.equal(run_gpu(mf, dl, x, ws=ws, poison=pat)["out"], first), f"run {i}"
     mf.close()
+
+
+def test_router_logits_have_fp32_accuracy(orc):
+    """Above 256 tokens the router is an MFMA GEMM over an exact three-way bf16 split
+    of the fp32 weights: its logits must be as close to the fp64 oracle as an fp32
+    dot product (a plain bf16 rounding of the weights would be off by ~1e-3)."""
+    dev = device()
+    shape, seed, T = synth.DECODE_BF16, 8, 512
+    dl = synth.make_layer_device(shape, seed, dev)
+    lc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dl.items()}
+    x = synth.make_tokens(shape, T, seed)
+    idx = np.arange(0, T, 16)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
+    got = run_gpu(mf, dl, x.to(dev))
+    ref = orc.forward(oracle_layer(lc), oracle_tokens(x[torch.from_numpy(idx)]), nthreads=oracle_threads())
+    err = np.max(np.abs(got["logits"][torch.from_numpy(idx)].double().numpy() - ref["logits"]))
+    gerr = np.max(np.abs(got["gate"][torch.from_numpy(idx)].double().numpy() - ref["gate"]))
+    print(f"  max |logit error| {err:.3e}, max |gate error| {gerr:.3e}", flush=True)
+    assert err <= 1e-5 and gerr <= 1e-6
+    mf.close()
