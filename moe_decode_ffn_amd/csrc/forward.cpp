@@ -108,9 +108,9 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
             P->occ_gg_gu[i] = gg_occupancy(true, 1 << i);
             P->occ_gg_d[i] = gg_occupancy(false, 1 << i);
         }
-        for (int i = 0; i < 2; ++i) {
-            P->occ_pf_gu[i] = pf_occupancy(true, 2 << i);
-            P->occ_pf_d[i] = pf_occupancy(false, 2 << i);
+        for (int i = 0; i < 3; ++i) {
+            P->occ_pf_gu[i] = pf_occupancy(true, 2 + i);
+            P->occ_pf_d[i] = pf_occupancy(false, 2 + i);
         }
     }
     P->ready = true;
@@ -299,10 +299,11 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     // are split into blocks of one pass
     const size_t mean_bucket = T * k / std::max<size_t>(1, std::min(E, T * k));
     const int gg_nt = mean_bucket >= 48 ? 4 : mean_bucket >= 24 ? 2 : 1;
-    // large buckets: the prefill GEMM (weight stages shared through LDS, 128 or 256 tokens
+    // large buckets: the prefill GEMM (weight stages shared through LDS, 128, 192 or 256 tokens
     // per pass)
     const bool pf = gemm && mean_bucket >= (size_t)kPfMinBucket;
-    const int pf_ntw = mean_bucket >= 160 ? 4 : 2;
+    // one pass per bucket where possible: 192 tokens cover buckets up to ~1.5x a mean of 128
+    const int pf_ntw = mean_bucket >= 192 ? 4 : mean_bucket >= 96 ? 3 : 2;
     const int gg_tb = (Ti + 16 * gg_nt - 1) / (16 * gg_nt);
     auto nt_index = [](int nt) { return nt <= 1 ? 0 : nt <= 2 ? 1 : 2; };
 
@@ -374,11 +375,13 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         g.tiles_routed = (int)(((gate_up ? I : H) + rows - 1) / rows);
         g.tiles_shared = shared ? (int)(((gate_up ? Is : H) + rows - 1) / rows) : 0;
         const int bn = pf_tokens_per_pass(pf_ntw);
-        const int jobs = g.tiles_shared * ((Ti + bn - 1) / bn) + (routed ? max_used * g.tiles_routed : 0);
-        const int occ = (gate_up ? P->occ_pf_gu : P->occ_pf_d)[pf_ntw >= 4 ? 1 : 0];
+        const int jobs = pf_job_count(g.tiles_shared, (Ti + bn - 1) / bn, routed ? max_used : 0, g.tiles_routed);
+        const int occ = (gate_up ? P->occ_pf_gu : P->occ_pf_d)[pf_ntw - 2];
         const int kid = routed ? (gate_up ? MOE_FFN_K_GG_GATE_UP : MOE_FFN_K_GG_DOWN)
                                : (gate_up ? MOE_FFN_K_SH_GATE_UP : MOE_FFN_K_SH_DOWN);
-        return timed(P, kid, s, [&] { return launch_pf(g, gate_up, pf_ntw, expert_grid(jobs, occ), s); });
+        // a multiple of 8 workgroups keeps job j on XCD j % 8 across the grid-stride loop
+        const int grid = std::max(8, expert_grid(jobs, occ) / 8 * 8);
+        return timed(P, kid, s, [&] { return launch_pf(g, gate_up, pf_ntw, grid, s); });
     };
     auto run_gg_gate_up = [&](hipStream_t s, bool routed, bool shared) {
         if (pf) return run_pf(s, true, routed, shared);

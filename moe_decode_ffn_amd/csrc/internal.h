@@ -89,7 +89,7 @@ struct moe_ffn_plan_s {
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
-    int occ_pf_gu[2] = {0, 0}, occ_pf_d[2] = {0, 0};        // prefill GEMM, 128/256 tokens per pass
+    int occ_pf_gu[3] = {0, 0, 0}, occ_pf_d[3] = {0, 0, 0};  // prefill GEMM, 128/192/256 tokens per pass
     bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
     // profiling
     bool profiling = false;
@@ -289,6 +289,7 @@ int pf_rows_per_job(bool gate_up);
 int pf_tokens_per_pass(int ntw);
 hipError_t launch_pf(const GGParams &p, bool gate_up, int ntw, int grid, hipStream_t s);
 int pf_occupancy(bool gate_up, int ntw);
+int pf_job_count(int tiles_shared, int n_tb, int nu, int tiles_routed);
 hipError_t launch_bucket_batch(const RouterParams &p, hipStream_t s);
 int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds);
 

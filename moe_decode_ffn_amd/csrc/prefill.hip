@@ -7,16 +7,20 @@
 // covers 64*NTW tokens of its bucket: each of the four waves owns 16*NTW of
 // the pass's tokens and all 128 rows.  K runs in stages of 64:
 //   * the weight stage (128 rows x 128 bytes) is loaded once per workgroup into
-//     LDS (double-buffered, rows padded to 144 bytes so the fragment reads hit
-//     distinct banks) and read by all four waves;
-//   * each wave loads its own token rows straight into registers, one stage
-//     ahead;
+//     LDS (double-buffered; 16-byte chunk c of row r sits at chunk position
+//     c ^ (r & 7), so the fragment reads hit distinct banks) and read by all four
+//     waves;
+//   * each wave loads its own token rows straight into registers; loads run two
+//     stages ahead in three register sets, and the barriers between stages order
+//     LDS only, so the prefetched loads stay in flight across them;
 //   * per 32-element K step a wave runs 8 x NTW v_mfma_f32_16x16x32_bf16.
 // The K order and the lane-to-K mapping are those of the smaller grouped GEMM
 // (32-element steps in ascending order, lane group g holding elements 8g..8g+7
 // of a step), so the two give the same bits.
 // Outputs as in the smaller GEMM: h in bf16 per (token, slot) pair or shared
 // token, y / S in fp32.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -29,12 +33,20 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfRows = 128;                        // weight rows per job
 constexpr int kPfBK = 64;                           // K elements per stage
-constexpr int kPfStride = kPfBK * 2 + 16;           // LDS bytes per weight row (padded)
+constexpr int kPfStride = kPfBK * 2;                // LDS bytes per weight row
 constexpr int kPfStage = kPfRows * kPfStride;       // LDS bytes per stage
 
 __device__ __forceinline__ floatx4_t pf_mfma(uint4 a, uint4 b, floatx4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Workgroup barrier ordering LDS accesses only: global loads in flight (the stages
+// prefetched ahead) are not waited for, as they would be by __syncthreads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 struct PfJob {
@@ -46,28 +58,42 @@ struct PfJob {
 };
 
 // Jobs: the shared expert's (row tile, token block) pairs first, then the row
-// tiles of every used expert (each walks its whole bucket in passes).
+// tiles of every used expert (each walks its whole bucket in passes).  Every job of
+// one token block or one expert runs on one XCD, so that the tokens its row tiles
+// all read come from that XCD's L2: with workgroups dispatched round-robin over the
+// 8 XCDs and a grid that is a multiple of 8, job j runs on XCD j % 8, and job j
+// belongs to block (or expert) 8 * (j / 8 / tiles) + j % 8, row tile (j / 8) % tiles.
+__host__ __device__ inline int pf_round8(int v) { return (v + 7) & ~7; }
+
+__host__ __device__ inline int pf_jobs(int tiles_shared, int n_tb, int nu, int tiles_routed) {
+    return tiles_shared * pf_round8(n_tb) + pf_round8(nu) * tiles_routed;
+}
+
 template <bool GU>
 __device__ __forceinline__ PfJob pf_decode(const GGParams &p, int j, int tb_len, int nu, int npairs) {
     PfJob jb{};
     jb.valid = false;
     const int n_tb = (p.T + tb_len - 1) / tb_len;
-    if (j < p.tiles_shared * n_tb) {
-        const int tb = j / p.tiles_shared;
+    const int shared_jobs = p.tiles_shared * pf_round8(n_tb);
+    if (j < shared_jobs) {
+        const int x = j & 7, r = j >> 3;
+        const int tb = 8 * (r / p.tiles_shared) + x;
+        if (tb >= n_tb) return jb;
         jb.valid = true;
         jb.routed = false;
         jb.W0 = p.sw0;
         jb.W1 = p.sw1;
         jb.K = GU ? p.H : p.Is;
         jb.rows = GU ? p.Is : p.H;
-        jb.tile = j - tb * p.tiles_shared;
+        jb.tile = r % p.tiles_shared;
         jb.tok0 = tb * tb_len;
         jb.ntok = min(tb_len, p.T - jb.tok0);
         jb.start = 0;
         return jb;
     }
-    j -= p.tiles_shared * n_tb;
-    const int slot = j / p.tiles_routed;
+    j -= shared_jobs;
+    const int x = j & 7, r = j >> 3;
+    const int slot = 8 * (r / p.tiles_routed) + x;
     if (slot >= nu) return jb;
     const int *rec = p.records + (size_t)slot * kRecInts;
     const int e = rec[0], start = rec[1], cnt = rec[2];
@@ -80,7 +106,7 @@ __device__ __forceinline__ PfJob pf_decode(const GGParams &p, int j, int tb_len,
     jb.W1 = GU ? p.w1 + m0 : nullptr;
     jb.K = K;
     jb.rows = rows;
-    jb.tile = j - slot * p.tiles_routed;
+    jb.tile = r % p.tiles_routed;
     jb.ntok = cnt;
     jb.tok0 = 0;
     jb.start = start;
@@ -96,7 +122,7 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
     const int T = p.T, k = p.k, npairs = T * k;
     int nu = p.routed ? *p.n_unique : 0;
     nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
-    const int J = p.tiles_shared * ((T + BN - 1) / BN) + nu * p.tiles_routed;
+    const int J = pf_jobs(p.tiles_shared, (T + BN - 1) / BN, nu, p.tiles_routed);
     // rows of the tile as a gate/up job sees them: 64 of gate, then the same 64 of up
     constexpr int kHalf = GU ? kPfRows / 2 : kPfRows;
 
@@ -107,14 +133,12 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
         const int nst = jb.K / kPfBK;
         // this thread's four 16-byte pieces of every weight stage: row u>>3, chunk u&7
         const uint8_t *asrc[4];
-        bool aok[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int u = tid + 256 * q, lr = u >> 3, ch = u & 7;
             const int half = lr / kHalf, r = jb.tile * kHalf + (lr - half * kHalf);
-            aok[q] = r < jb.rows;
             const uint8_t *W = half ? jb.W1 : jb.W0;
-            asrc[q] = W + (size_t)(aok[q] ? r : 0) * rb + ch * 16;
+            asrc[q] = W + (size_t)(r < jb.rows ? r : 0) * rb + ch * 16;
         }
         const uint8_t *bbase = GU ? (const uint8_t *)p.x
                                   : (const uint8_t *)(jb.routed ? (const void *)p.hb : (const void *)p.shb);
@@ -122,19 +146,17 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
         for (int t0 = 0; t0 < jb.ntok; t0 += BN) {
             // this lane's token rows (B side) and output rows, one per 16-token tile
             const uint8_t *brow[NTW];
-            bool bok[NTW];
             int orow[NTW];
 #pragma unroll
             for (int n = 0; n < NTW; ++n) {
                 const int a = t0 + wave * 16 * NTW + 16 * n + ri;
-                bok[n] = a < jb.ntok;
                 int src = 0, o = -1;
-                if (bok[n]) {
+                if (a < jb.ntok) {
                     if (jb.routed) {
                         const int pr = p.pairs[jb.start + a];
-                        bok[n] = pr >= 0 && pr < npairs;
-                        o = bok[n] ? pr : -1;
-                        src = bok[n] ? (GU ? pr / k : pr) : 0;
+                        const bool ok = pr >= 0 && pr < npairs;
+                        o = ok ? pr : -1;
+                        src = ok ? (GU ? pr / k : pr) : 0;
                     } else {
                         o = jb.tok0 + a;
                         src = o;
@@ -150,63 +172,72 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) acc[m][n] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-            // stage 0: weights to LDS buffer 0, tokens to registers
-            uint4 areg[4], b[NTW][2], nb[NTW][2];
+            // three register sets in rotation: stage s is loaded two stages ahead, its
+            // weights go to LDS slot s % 2 one stage ahead, its tokens feed the MFMAs
+            uint4 areg[3][4], breg[3][NTW][2];
+            auto load = [&](auto SI, int st) {
+                constexpr int i = decltype(SI)::value;
+                const size_t ko = (size_t)st * kPfBK * 2;
+                // unconditional (branch-free) loads: rows past the end read a clamped row,
+                // and the epilogue stores neither their rows nor their token columns
 #pragma unroll
-            for (int q = 0; q < 4; ++q) areg[q] = aok[q] ? ld16(asrc[q]) : make_uint4(0, 0, 0, 0);
+                for (int q = 0; q < 4; ++q) areg[i][q] = ld16(asrc[q] + ko);
 #pragma unroll
-            for (int n = 0; n < NTW; ++n)
+                for (int n = 0; n < NTW; ++n)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    b[n][s] = bok[n] ? ld16(brow[n] + (size_t)(32 * s + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
-            __syncthreads();  // the previous pass's readers are done with both buffers
+                    for (int s = 0; s < 2; ++s) breg[i][n][s] = ld16(brow[n] + ko + (size_t)(32 * s + 8 * g) * 2);
+            };
+            auto stash = [&](auto SI, int st) {  // weights of stage st into LDS slot st % 2
+                constexpr int i = decltype(SI)::value;
+                uint8_t *dst = lds + (st & 1) * kPfStage;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int u = tid + 256 * q;
-                *reinterpret_cast<uint4 *>(lds + (u >> 3) * kPfStride + (u & 7) * 16) = areg[q];
-            }
-            __syncthreads();
-
-            for (int st = 0; st < nst; ++st) {
-                const bool more = st + 1 < nst;
-                const uint8_t *cur = lds + (st & 1) * kPfStage;
-                if (more) {
-                    const size_t ko = (size_t)(st + 1) * kPfBK * 2;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) areg[q] = aok[q] ? ld16(asrc[q] + ko) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                        for (int s = 0; s < 2; ++s)
-                            nb[n][s] = bok[n] ? ld16(brow[n] + ko + (size_t)(32 * s + 8 * g) * 2)
-                                              : make_uint4(0, 0, 0, 0);
+                for (int q = 0; q < 4; ++q) {
+                    const int u = tid + 256 * q;
+                    *reinterpret_cast<uint4 *>(dst + (u >> 3) * kPfStride + (((u & 7) ^ ((u >> 3) & 7)) << 4)) = areg[i][q];
                 }
+            };
+            // one stage: prefetch stage st + 2, multiply stage st, stash stage st + 1.  The
+            // main loop issues its loads unconditionally so that the compiler's wait before
+            // each use counts only the loads issued after it (a conditional load makes it
+            // wait for all of them); the last few stages go through the guarded tail.
+            auto body = [&](auto SI, int st, bool fetch, bool keep) {
+                constexpr int i = decltype(SI)::value;
+                if (fetch) load(std::integral_constant<int, (i + 2) % 3>{}, st + 2);
+                const uint8_t *cur = lds + (st & 1) * kPfStage;
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     uint4 a[8];
 #pragma unroll
                     for (int m = 0; m < 8; ++m)
-                        a[m] = *reinterpret_cast<const uint4 *>(cur + (16 * m + ri) * kPfStride + (32 * s + 8 * g) * 2);
+                        a[m] = *reinterpret_cast<const uint4 *>(cur + (16 * m + ri) * kPfStride +
+                                                                (((4 * s + g) ^ ((16 * m + ri) & 7)) << 4));
 #pragma unroll
                     for (int n = 0; n < NTW; ++n)
 #pragma unroll
-                        for (int m = 0; m < 8; ++m) acc[m][n] = pf_mfma(a[m], b[n][s], acc[m][n]);
+                        for (int m = 0; m < 8; ++m) acc[m][n] = pf_mfma(a[m], breg[i][n][s], acc[m][n]);
                 }
-                if (more) {
-                    uint8_t *nxt = lds + ((st + 1) & 1) * kPfStage;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int u = tid + 256 * q;
-                        *reinterpret_cast<uint4 *>(nxt + (u >> 3) * kPfStride + (u & 7) * 16) = areg[q];
-                    }
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        b[n][0] = nb[n][0];
-                        b[n][1] = nb[n][1];
-                    }
-                }
-                __syncthreads();
+                if (keep) stash(std::integral_constant<int, (i + 1) % 3>{}, st + 1);
+                lds_barrier();
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            lds_barrier();  // every wave is done with both LDS slots (previous pass or job)
+            load(I0{}, 0);
+            load(I1{}, 1);  // K is a multiple of 128: at least two stages
+            stash(I0{}, 0);
+            lds_barrier();
+            int st = 0;
+            for (; st + 4 < nst; st += 3) {
+                body(I0{}, st, true, true);
+                body(I1{}, st + 1, true, true);
+                body(I2{}, st + 2, true, true);
             }
+            // tail: at most four stages, set index continuing from st % 3 == 0
+            body(I0{}, st, st + 2 < nst, st + 1 < nst);
+            if (st + 1 < nst) body(I1{}, st + 1, st + 3 < nst, st + 2 < nst);
+            if (st + 2 < nst) body(I2{}, st + 2, st + 4 < nst, st + 3 < nst);
+            if (st + 3 < nst) body(I0{}, st + 3, false, false);
 
             // epilogue: lane holds rows 16m + 4g + v of the tile for token column ri
             if constexpr (GU) {
@@ -251,6 +282,9 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
 }  // namespace
 
 size_t pf_lds_bytes() { return 2 * (size_t)kPfStage; }
+int pf_job_count(int tiles_shared, int n_tb, int nu, int tiles_routed) {
+    return pf_jobs(tiles_shared, n_tb, nu, tiles_routed);
+}
 int pf_rows_per_job(bool gate_up) { return gate_up ? kPfRows / 2 : kPfRows; }
 int pf_tokens_per_pass(int ntw) { return 64 * ntw; }
 
@@ -259,9 +293,11 @@ hipError_t launch_pf(const GGParams &p, bool gate_up, int ntw, int grid, hipStre
     const size_t lds = pf_lds_bytes();
     if (gate_up) {
         if (ntw <= 2) launch_kernel(k_pf<true, 2>, dim3(grid), dim3(256), lds, s, p);
+        else if (ntw == 3) launch_kernel(k_pf<true, 3>, dim3(grid), dim3(256), lds, s, p);
         else launch_kernel(k_pf<true, 4>, dim3(grid), dim3(256), lds, s, p);
     } else {
         if (ntw <= 2) launch_kernel(k_pf<false, 2>, dim3(grid), dim3(256), lds, s, p);
+        else if (ntw == 3) launch_kernel(k_pf<false, 3>, dim3(grid), dim3(256), lds, s, p);
         else launch_kernel(k_pf<false, 4>, dim3(grid), dim3(256), lds, s, p);
     }
     return hipGetLastError();
@@ -272,11 +308,13 @@ int pf_occupancy(bool gate_up, int ntw) {
     const size_t lds = pf_lds_bytes();
     hipError_t e;
     if (gate_up)
-        e = ntw <= 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 2>, 256, lds)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 4>, 256, lds);
+        e = ntw <= 2   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 2>, 256, lds)
+            : ntw == 3 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 3>, 256, lds)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 4>, 256, lds);
     else
-        e = ntw <= 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 2>, 256, lds)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 4>, 256, lds);
+        e = ntw <= 2   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 2>, 256, lds)
+            : ntw == 3 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 3>, 256, lds)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 4>, 256, lds);
     return e == hipSuccess && n > 0 ? n : 1;
 }
 
