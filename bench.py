@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "MoE-layer decode tokens/s at batch 1/8 + expert-weight HBM GB/s vs peak"
 LAYER_COPIES = {"bf16": 16, "q4": 32, "f32": 16}
 TOKEN_POOL = 8
@@ -174,6 +175,16 @@ def main() -> int:
     avg_us = ms_tot * 1e3 / max(1, n_launch)
     gu_units = unique_mean + (1 if shared_mode == "fused" else 0)
     achieved = gu_units * gu_b / (avg_us * 1e-6) / 1e9
+    # the contraction the dominant launch performs: gate and up (two H x I products) per
+    # (token, slot) pair, plus the shared expert's per token when it is fused in
+    gu_flops = 4.0 * shape.hidden * shape.inter * T * shape.top_k
+    if shared_mode == "fused":
+        gu_flops += 4.0 * shape.hidden * shape.shared_inter * T
+    tflops = gu_flops / (avg_us * 1e-6) / 1e12
+    # which roof binds the algorithm: the time its bytes take at peak bandwidth or the
+    # time its flops take at the MFMA peak (only the grouped GEMM runs on MFMA)
+    mfma_bound = dominant == "gg_gate_up" and (gu_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                                               > gu_units * gu_b / (HBM_PEAK_GBPS * 1e9))
     kernels = {k: round(v[0] * 1e3 / v[1], 3) for k, v in prof.items() if v[1]}
 
     # HBM bytes per launch of the dominant kernel from rocprofv3 counters, valid
@@ -183,7 +194,7 @@ def main() -> int:
     if (rec and rec.get("kernel_source_hash") == kernel_source_hash()
             and rec.get("workload") == args.workload and rec.get("shared_mode") == shared_mode
             and not args.input_block and T == counts[-1]
-            and dominant in str(rec.get("kernel", ""))):
+            and rec.get("kernel_id") == dominant):
         traffic = rec.get("hbm_bytes_per_launch")
 
     # ---- the oracle on the host cores (a bounded sample of the same workload) ----------------
@@ -198,16 +209,18 @@ def main() -> int:
         orc = Oracle()
         host_layer = oracle_layer({k: (v.cpu() if isinstance(v, torch.Tensor) else v)
                                    for k, v in layers[0].items()})
+        # each token's output depends on that token alone: large batches are sampled
+        n_cpu = min(T, 64)
         calls, c0 = 0, time.perf_counter()
         while True:
-            orc.forward(host_layer, oracle_tokens(xs[calls % TOKEN_POOL].cpu()), nthreads=cores)
+            orc.forward(host_layer, oracle_tokens(xs[calls % TOKEN_POOL][:n_cpu].cpu()), nthreads=cores)
             calls += 1
             if time.perf_counter() - c0 >= args.cpu_seconds:
                 break
         c_el = time.perf_counter() - c0
-        cpu = {"value": round(T * calls / c_el, 3), "unit": "tokens/s", "cores": cores,
+        cpu = {"value": round(n_cpu * calls / c_el, 3), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"{calls} forwards of {T} token(s) on layer copy 0 ({c_el:.1f} s, fp64, "
+               "sample": f"{calls} forwards of {n_cpu} token(s) on layer copy 0 ({c_el:.1f} s, fp64, "
                          f"{cores} OpenMP threads over rows)"}
 
     res = {
@@ -235,10 +248,16 @@ def main() -> int:
         "unique_experts_per_step": round(unique_mean, 3),
         "expert_weight_bytes_per_step": int(bytes_per_step),
         "kernel_avg_us": kernels,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "avg_us": round(avg_us, 3),
-                     "algorithmic_bytes_per_launch": int(gu_units * gu_b)},
+        "roofline": ({"bound": "mfma", "kernel": dominant, "achieved": round(tflops, 1),
+                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)} if mfma_bound else
+                     {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)})
+        | {"traffic": traffic, "avg_us": round(avg_us, 3),
+           "algorithmic_bytes_per_launch": int(gu_units * gu_b),
+           "algorithmic_flops_per_launch": int(gu_flops),
+           "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+           "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if dominant == "gg_gate_up" else None},
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }

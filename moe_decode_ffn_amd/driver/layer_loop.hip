@@ -4,7 +4,7 @@
 //
 //   layer_loop <workload> [mode] [steps] [warmup]
 //     workload: decode_bf16_t1 | decode_bf16_t8 | decode_q4_t1_t4 | decode_bf16_t128 |
-//               prefill_bf16_t4096 | tiny_fp32
+//               prefill_bf16_t4096 | prefill_bf16_t16384 | tiny_fp32
 //     mode:     auto | aux | seq | fused          (default auto)
 //
 // Weights and tokens are hash-filled on the device (a fixed seed per layer
@@ -83,6 +83,7 @@ const Workload kWorkloads[] = {
     {"decode_q4_t1_t4", 2048, 256, 8, 512, 512, 4, MOE_FFN_BF16, MOE_FFN_Q4_B32},
     {"decode_bf16_t128", 2048, 256, 8, 512, 512, 128, MOE_FFN_BF16, MOE_FFN_BF16},
     {"prefill_bf16_t4096", 2048, 256, 8, 512, 512, 4096, MOE_FFN_BF16, MOE_FFN_BF16},
+    {"prefill_bf16_t16384", 2048, 256, 8, 512, 512, 16384, MOE_FFN_BF16, MOE_FFN_BF16},
 };
 
 size_t elem_bytes(int dtype) { return dtype == MOE_FFN_F32 ? 4 : 2; }

@@ -78,8 +78,9 @@ WORKLOADS = {
     "decode_bf16_t8": (DECODE_BF16, 2, (8,)),
     "decode_q4_t1_t4": (DECODE_Q4, 3, (1, 4)),
     "decode_bf16_t128": (DECODE_BF16, 4, (128,)),
-    # a prefill chunk: every expert busy, ~128 tokens per expert
+    # prefill chunks: every expert busy, ~128 and ~512 tokens per expert
     "prefill_bf16_t4096": (DECODE_BF16, 5, (4096,)),
+    "prefill_bf16_t16384": (DECODE_BF16, 6, (16384,)),
 }
 
 

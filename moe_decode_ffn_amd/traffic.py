@@ -10,7 +10,7 @@ here launches a kernel of the layer):
 
     python -m moe_decode_ffn_amd.traffic summarize --fetch DIR --write DIR \\
         --cal-fetch DIR --cal-write DIR --cal-mib N --kernel REGEX \\
-        --workload NAME --shared-mode MODE --out profiles/traffic_<workload>.md
+        --workload NAME --shared-mode MODE --kernel-id ID --out profiles/traffic_<workload>.md
         [--extra DIR ...]
         Averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over the
         dispatches of the kernel, scales each by the copy's factor, and writes
@@ -135,6 +135,7 @@ def cmd_summarize(args) -> int:
         f"workload: {args.workload}",
         f"shared_mode: {args.shared_mode}",
         f"kernel: {args.kernel}",
+        f"kernel_id: {args.kernel_id}",
         f"kernel_source_hash: {kernel_source_hash()}",
         f"hbm_bytes_per_launch: {int(round(fetch_b + write_b))}",
         f"fetch_bytes_per_launch: {int(round(fetch_b))}",
@@ -176,6 +177,8 @@ def main(argv=None) -> int:
         s.add_argument(a, required=True)
     s.add_argument("--cal-mib", type=int, required=True)
     s.add_argument("--shared-mode", required=True, help="aux, seq or fused: the bench mode measured")
+    s.add_argument("--kernel-id", required=True,
+                   help="the profiling id of the kernel (moe_ffn_kernel_id name, e.g. gate_up, gg_gate_up)")
     s.add_argument("--extra", action="append")
     s.add_argument("--command", action="append", help="a command line to record in the summary")
     args = ap.parse_args(argv)
