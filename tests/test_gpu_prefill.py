@@ -157,3 +157,20 @@ def test_router_logits_have_fp32_accuracy(orc):
     print(f"  max |logit error| {err:.3e}, max |gate error| {gerr:.3e}", flush=True)
     assert err <= 1e-5 and gerr <= 1e-6
     mf.close()
+
+
+def test_prefill_gemm_gives_the_bits_of_the_small_gemm():
+    """The prefill GEMM takes over from a mean bucket of 32 tokens (128 tokens of this
+    layer: 12 experts, top-3); it walks K in the same order with the same lane mapping
+    as the smaller grouped GEMM, so the 127 tokens shared by a 127- and a 128-token
+    batch (one below, one at the switch) get the same bits."""
+    dev = device()
+    shape = synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16")
+    dl = synth.layer_to(synth.make_layer(shape, 48), dev)
+    x = synth.make_tokens(shape, 128, 48).to(dev)
+    mf = ffn.MoeFfn.for_shape(shape, max_tokens=128)
+    small = run_gpu(mf, dl, x[:127].contiguous())
+    big = run_gpu(mf, dl, x)
+    assert torch.equal(small["ids"], big["ids"][:127])
+    assert torch.equal(small["out"], big["out"][:127])
+    mf.close()
