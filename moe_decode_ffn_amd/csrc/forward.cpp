@@ -328,7 +328,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     const uint64_t delay_ticks = 20000;  // 200 us of the 100 MHz constant clock
 
     // large batches of bf16 tokens without the input norm: the router as an MFMA GEMM
-    const bool router_mfma = batch_route && rp.x_bf16 && !norm && H % 32 == 0;
+    const bool router_mfma = batch_route && rp.x_bf16 && !norm && H % 128 == 0;
     auto run_router = [&](hipStream_t s) {
         hipError_t e1 = timed(P, MOE_FFN_K_ROUTER, s, [&] {
             return router_mfma ? launch_router_mfma(rp, s) : launch_router(rp, P->map_router, r_grid, r_tiles, s);

@@ -249,64 +249,73 @@ __device__ __forceinline__ void split3(const float4 &u, const float4 &v, uint4 &
 }
 
 constexpr int kRgRows = 64;    // rows per workgroup (16 per wave)
-constexpr int kRgTokens = 64;  // tokens per workgroup (four 16-token tiles per wave)
 
+// One K step (32 elements) of a wave: its 16 weight rows (8 fp32 per lane) and its
+// token tiles (8 bf16 per lane each).  Steps are loaded two ahead in three register
+// sets; the main loop loads unconditionally (clamped rows and tokens are read and
+// never stored) so that each wait counts only the loads issued after the one it needs.
+template <int NT>  // 16-token tiles per wave (each workgroup: 16 * NT tokens)
+struct RgStep {
+    float4 wa, wb;
+    uint4 b[NT];
+};
+
+template <int NT>
 __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
+    constexpr int kRgTiles = NT, kRgTokens = 16 * NT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = lane & 15, g = lane >> 4;
     const int H = p.H, E = p.E, T = p.T;
     if (p.bcount && blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = tid; i < 2 * E; i += 256) p.bcount[i] = 0;  // counts and cursors
     const int row = blockIdx.x * kRgRows + wave * 16 + ri;      // A row of this lane
-    const bool rok = row <= E;
-    const float *W = row < E ? p.router + (size_t)row * H : p.gate_vec;
+    const float *W = (row < E ? p.router + (size_t)row * H : p.gate_vec) + 8 * g;
     const int t0 = blockIdx.y * kRgTokens;
-    const uint16_t *xb[4];
-    bool tok_ok[4];
+    const uint16_t *xb[kRgTiles];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kRgTiles; ++n) {
         const int t = t0 + 16 * n + ri;
-        tok_ok[n] = t < T;
-        xb[n] = reinterpret_cast<const uint16_t *>(p.x) + (size_t)(tok_ok[n] ? t : 0) * H;
+        xb[n] = reinterpret_cast<const uint16_t *>(p.x) + (size_t)(t < T ? t : 0) * H + 8 * g;
     }
-    rfloatx4_t acc[4];
+    rfloatx4_t acc[kRgTiles];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[n] = rfloatx4_t{0.f, 0.f, 0.f, 0.f};
-    float4 wa, wb, nwa, nwb;
-    uint4 b[4], nb[4];
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    wa = rok ? *reinterpret_cast<const float4 *>(W + 8 * g) : z4;
-    wb = rok ? *reinterpret_cast<const float4 *>(W + 8 * g + 4) : z4;
+    for (int n = 0; n < kRgTiles; ++n) acc[n] = rfloatx4_t{0.f, 0.f, 0.f, 0.f};
+    RgStep<NT> st[3];
+    auto load = [&](RgStep<NT> &d, int s) {
+        const int ko = 32 * s;
+        d.wa = *reinterpret_cast<const float4 *>(W + ko);
+        d.wb = *reinterpret_cast<const float4 *>(W + ko + 4);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) b[n] = tok_ok[n] ? ld16(xb[n] + 8 * g) : make_uint4(0, 0, 0, 0);
-    const int nstep = H / 32;
-    for (int s = 0; s < nstep; ++s) {
-        const bool more = s + 1 < nstep;
-        if (more) {
-            const int ko = 32 * (s + 1) + 8 * g;
-            nwa = rok ? *reinterpret_cast<const float4 *>(W + ko) : z4;
-            nwb = rok ? *reinterpret_cast<const float4 *>(W + ko + 4) : z4;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) nb[n] = tok_ok[n] ? ld16(xb[n] + ko) : make_uint4(0, 0, 0, 0);
-        }
+        for (int n = 0; n < kRgTiles; ++n) d.b[n] = ld16(xb[n] + ko);
+    };
+    auto mul = [&](const RgStep<NT> &d) {
         uint4 hi, mid, lo;
-        split3(wa, wb, hi, mid, lo);
+        split3(d.wa, d.wb, hi, mid, lo);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            acc[n] = r_mfma(hi, b[n], acc[n]);
-            acc[n] = r_mfma(mid, b[n], acc[n]);
-            acc[n] = r_mfma(lo, b[n], acc[n]);
+        for (int n = 0; n < kRgTiles; ++n) {
+            acc[n] = r_mfma(hi, d.b[n], acc[n]);
+            acc[n] = r_mfma(mid, d.b[n], acc[n]);
+            acc[n] = r_mfma(lo, d.b[n], acc[n]);
         }
-        if (more) {
-            wa = nwa;
-            wb = nwb;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) b[n] = nb[n];
-        }
+    };
+    const int nstep = H / 32;  // a multiple of 4 (H is a multiple of 128 here)
+    load(st[0], 0);
+    load(st[1], 1);
+    int s = 0;
+    for (; s + 4 < nstep; s += 3) {
+        load(st[2], s + 2); mul(st[0]);
+        load(st[0], s + 3); mul(st[1]);
+        load(st[1], s + 4); mul(st[2]);
     }
+    // tail: at most four steps, sets continuing from s % 3 == 0
+    if (s + 2 < nstep) load(st[2], s + 2);
+    mul(st[0]);
+    if (s + 1 < nstep) { if (s + 3 < nstep) load(st[0], s + 3); mul(st[1]); }
+    if (s + 2 < nstep) mul(st[2]);
+    if (s + 3 < nstep) mul(st[0]);
     // lane holds rows 4g + v of the wave's 16 for token column ri
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kRgTiles; ++n) {
         const int t = t0 + 16 * n + ri;
         if (t >= T) continue;
 #pragma unroll
@@ -318,9 +327,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
 }
 
 hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s) {
-    if (!p.x_bf16 || p.norm_w || p.H % 32 != 0) return hipErrorInvalidValue;
-    const dim3 grid((p.E + 1 + kRgRows - 1) / kRgRows, (p.T + kRgTokens - 1) / kRgTokens);
-    launch_kernel(k_router_mfma, grid, dim3(256), 0, s, p);
+    if (!p.x_bf16 || p.norm_w || p.H % 128 != 0) return hipErrorInvalidValue;
+    // wider token blocks for big batches: fewer re-reads (and splits) of the weights
+    const int nt = p.T >= 4096 ? 4 : 2;
+    const dim3 grid((p.E + 1 + kRgRows - 1) / kRgRows, (p.T + 16 * nt - 1) / (16 * nt));
+    if (nt == 4) launch_kernel(k_router_mfma<4>, grid, dim3(256), 0, s, p);
+    else launch_kernel(k_router_mfma<2>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
