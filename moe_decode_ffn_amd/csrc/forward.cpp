@@ -338,6 +338,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         if (!batch_route) return e1;
         e1 = timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_rank_batch(rp, s); });
         if (e1 != hipSuccess) return e1;
+        e1 = timed(P, MOE_FFN_K_BUCKET, s, [&] { return launch_count_scan(rp, s); });
+        if (e1 != hipSuccess) return e1;
         return timed(P, MOE_FFN_K_BUCKET, s, [&] { return launch_bucket_batch(rp, s); });
     };
     // grid of a grid-stride expert launch: its jobs, capped at the resident workgroups

@@ -56,7 +56,7 @@ struct Layout {
     size_t pos_expert = 0; // i32 [Tmax*k]: expert of each bucketed position
     size_t logits = 0;     // f32 [Tmax][E+1] (column E = shared-gate logit), router -> gate/up
     size_t xn = 0;         // x_dtype [Tmax][H]: normalised input (INPUT_NORM), router -> experts
-    size_t bcount = 0;     // i32 [4][E]: batch routing's per-expert count, cursor, offset, slot
+    size_t bcount = 0;     // i32: batch routing's totals [E], count rows [W][E], in-workgroup ranks [T*k]
     size_t routing_bytes = 0;
     // phase region: reused by the sequential steps
     size_t h = 0;       // gate/up -> down: f32 [Tmax*k][I]
@@ -130,9 +130,9 @@ struct RouterParams {
     const float *norm_w;    // [H] or NULL: no norm
     float norm_eps;
     void *xn;               // [T][H] x_dtype
-    // batch routing (large batches): workgroup (0, 0) zeroes the per-expert counts and
-    // cursors; k_rank_batch ranks and counts, k_bucket_batch scans and scatters
-    int *bcount;            // [4][E] or NULL
+    // batch routing (large batches): k_rank_batch ranks and counts per workgroup,
+    // k_count_scan turns the counts into prefixes, k_bucket_batch places the pairs
+    int *bcount;            // totals [E], count rows [W][E], in-workgroup ranks [T*k]; or NULL
 };
 
 struct GateUpParams {
@@ -282,6 +282,8 @@ size_t route_lds_bytes(int T, int k, int E);
 size_t route_kernel_lds_bytes(int T, int k, int E);
 hipError_t launch_route(const RouterParams &p, hipStream_t s);
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s);
+hipError_t launch_count_scan(const RouterParams &p, hipStream_t s);
+size_t batch_route_ints(int T, int k, int E);
 hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s);
 // prefill grouped GEMM (large buckets)
 size_t pf_lds_bytes();

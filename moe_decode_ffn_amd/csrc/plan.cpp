@@ -165,8 +165,8 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.logits = c;     c += align_up(T * (E + 1) * 4);
     // normalised input of both branches (x_dtype), router -> experts
     L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
-    // per-expert count, cursor, offset and slot of batch routing (batches above kTailMaxTokens)
-    L.bcount = c;     c += d.max_tokens > kTailMaxTokens ? align_up((size_t)4 * E * 4) : 0;
+    // batch routing's counts, prefixes and ranks (batches above kTailMaxTokens)
+    L.bcount = c;     c += d.max_tokens > kTailMaxTokens ? align_up(batch_route_ints(d.max_tokens, k, E) * 4) : 0;
     L.routing_bytes = c - L.shared_bytes;
     // sequential steps: gate/up holds h, down holds h and y, join holds y
     const size_t base = c;

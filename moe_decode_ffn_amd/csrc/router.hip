@@ -85,9 +85,6 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
                                        : make_float4(1.f, 1.f, 1.f, 1.f);
     }
 
-    if (p.bcount && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = tid; i < 2 * E; i += 256) p.bcount[i] = 0;  // counts and cursors
-
     const int t0 = blockIdx.y * p.tok_tile;
     const int nt = min(p.tok_tile, p.T - t0);
     // the normalised tokens of the tile are written by the column's workgroups in
@@ -266,8 +263,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = lane & 15, g = lane >> 4;
     const int H = p.H, E = p.E, T = p.T;
-    if (p.bcount && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = tid; i < 2 * E; i += 256) p.bcount[i] = 0;  // counts and cursors
     const int row = blockIdx.x * kRgRows + wave * 16 + ri;      // A row of this lane
     const float *W = (row < E ? p.router + (size_t)row * H : p.gate_vec) + 8 * g;
     const int t0 = blockIdx.y * kRgTokens;
@@ -337,43 +332,93 @@ hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s) {
 }
 
 // ---- batch routing (large batches) ----------------------------------------------------
-// k_rank_batch: each wave ranks kRankTokensPerWave tokens in turn and counts its picks
-// per expert (integer atomics: the counts are exact whatever the order).
+// Three launches, no atomics, a deterministic result: buckets hold their pairs in pair
+// order, as the one-workgroup bucketing of smaller batches does.
+//   k_rank_batch    a workgroup ranks kRankTokensPerWg tokens (one wave per token in
+//                   turn), writes its row of per-expert counts and, per pair, the
+//                   number of earlier pairs of the workgroup with the same expert;
+//   k_count_scan    per expert, the exclusive prefix of the count rows (in place) and
+//                   the expert's total;
+//   k_bucket_batch  every workgroup scans the totals (expert offsets, used-expert
+//                   slots); workgroup 0 writes the job records; each pair goes to
+//                   offset + prefix of its workgroup + its rank inside the workgroup.
+// bcount layout (ints): totals [E], then the count rows [W][E] (W = ceil(T / 16)),
+// then the in-workgroup ranks [T*k].
 constexpr int kRankTokensPerWave = 4;
 constexpr int kRankTokensPerWg = 4 * kRankTokensPerWave;
+constexpr int kRankPairsMax = kRankTokensPerWg * kMaxTopK;
 
 __global__ __launch_bounds__(256) void k_rank_batch(RouterParams p) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int s_ids[kRankPairsMax];
+    __shared__ int s_hist[kMaxExperts];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = p.E, k = p.k;
-    int *cnt = p.bcount;
+    const int tw0 = blockIdx.x * kRankTokensPerWg;
+    const int ntw = min(kRankTokensPerWg, p.T - tw0);
+    for (int e = tid; e < E; e += 256) s_hist[e] = 0;
     for (int i = 0; i < kRankTokensPerWave; ++i) {
-        const int t = blockIdx.x * kRankTokensPerWg + i * 4 + wave;
-        if (t >= p.T) break;
+        const int lt = i * 4 + wave, t = tw0 + lt;
+        if (lt >= ntw) break;
         RouteOut o{p.ids + (size_t)t * k, p.wts + (size_t)t * k, p.gate_s + t,
                    p.dbg_ids ? p.dbg_ids + (size_t)t * k : nullptr, p.dbg_w ? p.dbg_w + (size_t)t * k : nullptr,
                    p.dbg_gate ? p.dbg_gate + t : nullptr, p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
         route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
-        if (lane < k) {
-            const int e = o.ids[lane];  // this lane's own store: visible to it
-            if (e >= 0 && e < E) atomicAdd(cnt + e, 1);
-        }
+        if (lane < k) s_ids[lt * k + lane] = o.ids[lane];  // this lane's own store
     }
+    __syncthreads();
+    const int np = ntw * k;
+    int *rank = p.bcount + E + (size_t)gridDim.x * E;
+    for (int q = tid; q < np; q += 256) {
+        const int e = s_ids[q];
+        int r = 0;
+        for (int j = 0; j < q; ++j) r += s_ids[j] == e ? 1 : 0;
+        rank[(size_t)tw0 * k + q] = r;
+        if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);  // LDS: exact whatever the order
+    }
+    __syncthreads();
+    int *row = p.bcount + E + (size_t)blockIdx.x * E;
+    for (int e = tid; e < E; e += 256) row[e] = s_hist[e];
 }
 
-// k_bucket_batch: every workgroup scans the counts (expert offsets, used-expert
-// slots) in LDS; workgroup 0 writes the job records and the used-expert count;
-// every workgroup places its pairs, each at its expert's offset plus a cursor
-// taken atomically.  Within an expert the order of the pairs depends on timing,
-// but no result does: every pair's rows are computed alone and the join sums a
-// token's slots in slot order.
+// one workgroup per expert: exclusive prefix of its column over the W count rows
+__global__ __launch_bounds__(256) void k_count_scan(RouterParams p, int W) {
+    __shared__ int s_wsum[4];
+    const int e = blockIdx.x, E = p.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int *col = p.bcount + E + e;
+    const int per = (W + 255) / 256, w0 = tid * per;
+    int a = 0;
+    for (int i = 0; i < per; ++i)
+        if (w0 + i < W) a += col[(size_t)(w0 + i) * E];
+    int ia = a;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(ia, d);
+        if (lane >= d) ia += y;
+    }
+    if (lane == 63) s_wsum[wave] = ia;
+    __syncthreads();
+    int base = ia - a;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    for (int i = 0; i < per; ++i)
+        if (w0 + i < W) {
+            int *c = col + (size_t)(w0 + i) * E;
+            const int v = *c;
+            *c = base;
+            base += v;
+        }
+    if (tid == 255) p.bcount[e] = base;  // the last thread ends on the total
+}
+
 constexpr int kBucketPairsPerWg = 1024;
 
 __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
     __shared__ int s_off[kMaxExperts], s_slot[kMaxExperts], s_wsum[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = p.E, NP = p.T * p.k;
+    const int E = p.E, NP = p.T * p.k, k = p.k;
     const int *cnt = p.bcount;
-    int *cur = p.bcount + E;
+    const int *pre = p.bcount + E;
+    const int W = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    const int *rank = p.bcount + E + (size_t)W * E;
     // exclusive scans of cnt[] and (cnt[] > 0): thread owns two consecutive experts
     const int e0 = 2 * tid;
     const int c0 = e0 < E ? cnt[e0] : 0, c1 = e0 + 1 < E ? cnt[e0 + 1] : 0;
@@ -405,18 +450,31 @@ __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
     for (int q = blockIdx.x * kBucketPairsPerWg + tid; q < q_end; q += 256) {
         const int e = p.ids[q];
         if (e < 0 || e >= E) continue;
-        const int r = atomicAdd(cur + e, 1);
+        const int w = (q / k) / kRankTokensPerWg;
+        const int r = pre[(size_t)w * E + e] + rank[q];  // place inside the expert's bucket
         const int pos = s_off[e] + r;
-        if (r >= cnt[e] || pos >= NP) continue;  // only with a corrupt count
+        if (r >= cnt[e] || pos >= NP) continue;  // only with corrupt counts
         p.pairs[pos] = q;
         p.pos_expert[pos] = e;
         if (r < kRecPairs) p.records[(size_t)s_slot[e] * kRecInts + 4 + r] = q;
     }
 }
 
+size_t batch_route_ints(int T, int k, int E) {
+    const size_t W = (T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    return (size_t)E + W * E + (size_t)T * k;
+}
+
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s) {
     const int grid = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    if (p.k > kMaxTopK || p.E > kMaxExperts) return hipErrorInvalidValue;
     launch_kernel(k_rank_batch, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_scan(const RouterParams &p, hipStream_t s) {
+    const int W = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    launch_kernel(k_count_scan, dim3(p.E), dim3(256), 0, s, p, W);
     return hipGetLastError();
 }
 

@@ -170,14 +170,16 @@ def test_plan_rejects_bad_norm_eps(lib, eps):
 
 @pytest.mark.parametrize("T", [257, 4096])
 def test_workspace_with_batch_routing(lib, T):
-    # above 256 tokens the routing region also holds four per-expert int arrays
-    # (count, cursor, offset, slot) for the ranking and bucketing launches
+    # above 256 tokens the routing region also holds the bucketing launches' ints:
+    # per-expert totals, one count row per ranking workgroup of 16 tokens, and each
+    # pair's rank inside its workgroup
     H, E, k, I, Is = 2048, 256, 8, 512, 512
     plan, ws = ffn.moe_ffn_plan(desc(max_tokens=T))
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
+    W = (T + 15) // 16
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(4 * E * 4))
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align((E + W * E + T * k) * 4))
     assert info.routing_region_bytes == routing
     assert ws == info.workspace_bytes == (_align(T * Is * 4) + _align(T * H * 4) + routing
                                           + _align(T * k * I * 4) + _align(T * k * H * 4))
