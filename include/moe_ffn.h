@@ -203,7 +203,8 @@ typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up (routed, or routed + shared when fused) */
     MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN_JOIN = 9,    /* mat-vec regime: down of every pair of a row tile + the join */
-    MOE_FFN_K_BUCKET = 10,      /* above 256 tokens: bucketing of the ranked pairs by expert */
+    MOE_FFN_K_BUCKET = 10,      /* above 256 tokens: bucketing of the ranked pairs by expert (two
+                                   launches: the per-expert scan of the counts, the placement) */
     MOE_FFN_K_COUNT = 11
 } moe_ffn_kernel_id;
 

@@ -269,8 +269,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     // else a routing launch of its own (one wave per token) or the router's tail
     const bool route_kernel = !gp.route_here && Ti <= kRouteKernelMax &&
                               route_kernel_lds_bytes(Ti, (int)k, (int)E) <= kLdsLimit;
-    // large batches: ranking and bucketing launches of their own, through global memory
-    const bool batch_route = Ti > kTailMaxTokens;
+    // large batches (or a routing tail that does not fit in LDS): ranking and bucketing
+    // launches of their own, through global memory
+    const bool batch_route = Ti > kTailMaxTokens || (!gp.route_here && !route_kernel && !P->tail_ok);
     rp.route_tail = gp.route_here || route_kernel || batch_route ? 0 : 1;
     rp.bcount = batch_route ? (int *)(W + L.bcount) : nullptr;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);

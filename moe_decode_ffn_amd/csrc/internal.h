@@ -91,6 +91,7 @@ struct moe_ffn_plan_s {
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
     int occ_pf_gu[3] = {0, 0, 0}, occ_pf_d[3] = {0, 0, 0};  // prefill GEMM, 128/192/256 tokens per pass
     bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
+    bool tail_ok = true;    // the router's LDS routing tail fits for every batch up to kTailMaxTokens
     // profiling
     bool profiling = false;
     std::vector<moeffn::ProfRec> prof;

@@ -143,12 +143,14 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     rq.H = H; rq.x_bf16 = xbytes == 2;
     rq.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
     const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
-    // LDS routing runs up to kTailMaxTokens tokens; larger batches route through global memory
-    if (!maps_ok || router_lds_bytes(rq) > kLdsLimit ||
-        route_lds_bytes(std::min(d.max_tokens, kTailMaxTokens), k, E) > kLdsLimit) {
+    if (!maps_ok || router_lds_bytes(rq) > kLdsLimit) {
         delete P;
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
     }
+
+    // the router's routing tail ranks and buckets up to kTailMaxTokens tokens in LDS; where
+    // that does not fit (many experts and picks), those batches take batch routing too
+    P->tail_ok = route_lds_bytes(std::min(d.max_tokens, kTailMaxTokens), k, E) <= kLdsLimit;
 
     Layout &L = P->L;
     size_t c = 0;
@@ -166,7 +168,8 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     // normalised input of both branches (x_dtype), router -> experts
     L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
     // batch routing's counts, prefixes and ranks (batches above kTailMaxTokens)
-    L.bcount = c;     c += d.max_tokens > kTailMaxTokens ? align_up(batch_route_ints(d.max_tokens, k, E) * 4) : 0;
+    const bool batch_possible = d.max_tokens > kTailMaxTokens || !P->tail_ok;
+    L.bcount = c;     c += batch_possible ? align_up(batch_route_ints(d.max_tokens, k, E) * 4) : 0;
     L.routing_bytes = c - L.shared_bytes;
     // sequential steps: gate/up holds h, down holds h and y, join holds y
     const size_t base = c;

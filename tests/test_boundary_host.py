@@ -185,6 +185,20 @@ def test_workspace_with_batch_routing(lib, T):
                                           + _align(T * k * I * 4) + _align(T * k * H * 4))
 
 
+def test_plan_with_no_room_for_the_lds_routing_tail(lib):
+    # 512 experts x top-32 at 100 tokens: the router's LDS routing tail would not fit, so
+    # the plan reserves batch routing's ints instead of refusing the shape
+    E, k, T = 512, 32, 100
+    plan, ws = ffn.moe_ffn_plan(desc(hidden=128, n_experts=E, top_k=k, inter=128, shared_inter=128,
+                                     max_tokens=T))
+    info = ffn.moe_ffn_plan_get_info(plan)
+    ffn.moe_ffn_destroy(plan)
+    W = (T + 15) // 16
+    routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align((E + W * E + T * k) * 4))
+    assert info.routing_region_bytes == routing
+
+
 def test_auto_mode_defaults(lib):
     plan, _ = ffn.moe_ffn_plan(desc())
     info = ffn.moe_ffn_plan_get_info(plan)
