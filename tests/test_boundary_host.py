@@ -186,9 +186,9 @@ def test_workspace_with_batch_routing(lib, T):
 
 
 def test_plan_with_no_room_for_the_lds_routing_tail(lib):
-    # 512 experts x top-32 at 100 tokens: the router's LDS routing tail would not fit, so
+    # 512 experts x top-32 at 256 tokens: the router's LDS routing tail would not fit, so
     # the plan reserves batch routing's ints instead of refusing the shape
-    E, k, T = 512, 32, 100
+    E, k, T = 512, 32, 256
     plan, ws = ffn.moe_ffn_plan(desc(hidden=128, n_experts=E, top_k=k, inter=128, shared_inter=128,
                                      max_tokens=T))
     info = ffn.moe_ffn_plan_get_info(plan)

@@ -32,8 +32,8 @@ SMALL = {
     "bf16_gemm_matvec_forced": (synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16"), 45, (300,),
                                 ffn.FORCE_MATVEC),
     # the largest expert count and top-k: 512 experts (two per scanning thread), 32 picks a
-    # token (512 pairs per ranking workgroup); the router's LDS routing tail does not fit,
-    # so 100 tokens take batch routing too (20 tokens: the routing launch)
+    # token (512 pairs per ranking workgroup); with room for 300 tokens the router's LDS
+    # routing tail does not fit, so 100 tokens take batch routing too (20: the routing launch)
     "bf16_e512_k32": (synth.LayerShape(128, 512, 32, 128, 128, "bf16", "bf16"), 49, (20, 100, 300), 0),
 }
 
