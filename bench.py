@@ -30,6 +30,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "MoE-layer decode tokens/s at batch 1/8 + expert-weight HBM GB/s vs peak"
 LAYER_COPIES = {"bf16": 16, "q4": 32, "f32": 16}
+MIN_ROTATION_BYTES = 512 << 20
 TOKEN_POOL = 8
 WINDOW_REPEATS = 4
 
@@ -84,7 +85,12 @@ def main() -> int:
             "fused": ffn.SHARED_FUSED}[args.mode]
 
     # ---- inputs resident in HBM -----------------------------------------------------
-    L = LAYER_COPIES[shape.w_dtype] if shape.hidden >= 1024 else 2
+    # enough copies that the calls between two uses of one copy read well over the 256 MB
+    # cache even at one token (k routed experts + the shared one per call)
+    gu_b, d_b = expert_bytes(shape)
+    min_call_bytes = (shape.top_k + 1) * (gu_b + d_b)
+    L = (max(LAYER_COPIES[shape.w_dtype], min(128, -(-MIN_ROTATION_BYTES // min_call_bytes) + 1))
+         if shape.hidden >= 1024 else 2)
     layers = [synth.make_layer_device(shape, 100 + i, dev) for i in range(L)]
     if args.input_block:
         layers = [synth.with_input_block(ly, 500 + i, eps=1e-6) for i, ly in enumerate(layers)]
@@ -113,7 +119,6 @@ def main() -> int:
         uniq.append(len(torch.unique(ids)))
     torch.cuda.synchronize()
     unique_mean = float(np.mean(uniq))
-    gu_b, d_b = expert_bytes(shape)
     bytes_per_step = unique_mean * (gu_b + d_b) + (gu_b + d_b)  # routed + shared expert weights
 
     # ---- graphs of whole rotation windows ----------------------------------------------------

@@ -4,7 +4,8 @@
 //
 //   layer_loop <workload> [mode] [steps] [warmup]
 //     workload: decode_bf16_t1 | decode_bf16_t8 | decode_q4_t1_t4 | decode_bf16_t128 |
-//               prefill_bf16_t4096 | prefill_bf16_t16384 | tiny_fp32
+//               prefill_bf16_t4096 | prefill_bf16_t16384 | decode_bf16_t1_tp8 |
+//               decode_bf16_t8_tp8 | tiny_fp32
 //     mode:     auto | aux | seq | fused          (default auto)
 //
 // Weights and tokens are hash-filled on the device (a fixed seed per layer
@@ -14,6 +15,7 @@
 // around the timed loop, synchronised at both ends).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cstdio>
 #include <cstdlib>
@@ -84,6 +86,9 @@ const Workload kWorkloads[] = {
     {"decode_bf16_t128", 2048, 256, 8, 512, 512, 128, MOE_FFN_BF16, MOE_FFN_BF16},
     {"prefill_bf16_t4096", 2048, 256, 8, 512, 512, 4096, MOE_FFN_BF16, MOE_FFN_BF16},
     {"prefill_bf16_t16384", 2048, 256, 8, 512, 512, 16384, MOE_FFN_BF16, MOE_FFN_BF16},
+    // one GPU's shard of the layer split eight ways inside every expert
+    {"decode_bf16_t1_tp8", 2048, 256, 8, 64, 64, 1, MOE_FFN_BF16, MOE_FFN_BF16},
+    {"decode_bf16_t8_tp8", 2048, 256, 8, 64, 64, 8, MOE_FFN_BF16, MOE_FFN_BF16},
 };
 
 size_t elem_bytes(int dtype) { return dtype == MOE_FFN_F32 ? 4 : 2; }
@@ -153,9 +158,15 @@ int main(int argc, char **argv) {
         return 1;
     }
 
-    // layer copies: enough that one copy's weights leave the 256 MB cache before reuse
+    // layer copies: enough that one copy's weights leave the 256 MB cache before reuse,
+    // even at one token (k routed experts and the shared one per call read 512 MiB
+    // between two uses of a copy)
     const size_t layer_bytes = mat_bytes(wd, (size_t)E * I, H) * 3 + mat_bytes(wd, Is, H) * 3;
-    const int copies = layer_bytes > ((size_t)64 << 20) ? (wd == MOE_FFN_Q4_B32 ? 32 : 16) : 2;
+    const size_t expert_bytes = mat_bytes(wd, I, H) * 3 + (wd == MOE_FFN_Q4_B32 ? (size_t)I * H / 32 * 2 * 3 : 0);
+    const size_t min_call = (size_t)(k + 1) * expert_bytes;
+    const int base = wd == MOE_FFN_Q4_B32 ? 32 : 16;
+    const int rot = (int)std::min<size_t>(128, (((size_t)512 << 20) + min_call - 1) / min_call + 1);
+    const int copies = layer_bytes > ((size_t)64 << 20) ? std::max(base, rot) : 2;
     std::vector<moe_ffn_tensors> ts(copies);
     void *x = dalloc((size_t)T * H * elem_bytes(wl->x_dtype));
     float *out = (float *)dalloc((size_t)T * H * 4);

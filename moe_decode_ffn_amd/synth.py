@@ -70,6 +70,10 @@ class LayerShape:
 TINY = LayerShape(64, 8, 2, 32, 32, "f32", "f32")
 DECODE_BF16 = LayerShape(2048, 256, 8, 512, 512, "bf16", "bf16")
 DECODE_Q4 = LayerShape(2048, 256, 8, 512, 512, "bf16", "q4")
+# one GPU's share of the decode layer split eight ways inside every expert (each GPU
+# holds 64 of the 512 intermediate rows of every expert and of the shared expert;
+# the router is replicated): the same kernels at the shard's real shape
+DECODE_BF16_TP8 = LayerShape(2048, 256, 8, 64, 64, "bf16", "bf16")
 
 WORKLOADS = {
     # name: (shape, seed, token counts)
@@ -81,6 +85,9 @@ WORKLOADS = {
     # prefill chunks: every expert busy, ~128 and ~512 tokens per expert
     "prefill_bf16_t4096": (DECODE_BF16, 5, (4096,)),
     "prefill_bf16_t16384": (DECODE_BF16, 6, (16384,)),
+    # one GPU's shard of the layer split eight ways inside every expert
+    "decode_bf16_t1_tp8": (DECODE_BF16_TP8, 7, (1,)),
+    "decode_bf16_t8_tp8": (DECODE_BF16_TP8, 9, (8,)),
 }
 
 

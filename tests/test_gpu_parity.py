@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from moe_decode_ffn_amd import ffn, synth
-from tests.gpu_common import compare, device, oracle_threads, run_gpu, tol_for
+from tests.gpu_common import TOL_LOWP, compare, device, oracle_threads, run_gpu, tol_for
 from tests.helpers import oracle_layer, oracle_tokens
 
 pytestmark = pytest.mark.gpu
@@ -127,6 +127,9 @@ FULL = {
     "decode_q4_t1": (synth.DECODE_Q4, 3, 1, 0),
     "decode_q4_t4": (synth.DECODE_Q4, 3, 4, 0),
     "decode_q4_t12": (synth.DECODE_Q4, 3, 12, 0),
+    # one GPU's shard of the layer split eight ways inside every expert (I = I_s = 64)
+    "decode_bf16_t1_tp8": (synth.DECODE_BF16_TP8, 7, 1, 0),
+    "decode_bf16_t8_tp8": (synth.DECODE_BF16_TP8, 9, 8, 0),
 }
 
 
@@ -175,6 +178,50 @@ def test_decode_bf16_t128(orc):
     rep = compare(orc, lc, x, run_gpu(mf, dl, x.to(dev)), tol_for(shape), ref=ref)
     print(f"  {rep}", flush=True)
     mf.close()
+
+
+def _shard(layer: dict, r0: int, r1: int) -> dict:
+    """Rows r0:r1 of the intermediate dimension of every expert and of the shared expert."""
+    s = layer["shape"]
+    out = dict(layer)
+    out["shape"] = s.with_(inter=r1 - r0, shared_inter=r1 - r0)
+    for name in ("gate", "up", "sh_gate", "sh_up"):
+        out[name] = layer[name][..., r0:r1, :].contiguous()
+    for name in ("down", "sh_down"):
+        out[name] = layer[name][..., r0:r1].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_tp8_shards_sum_to_the_layer(orc, T):
+    """The layer split eight ways inside every expert (each shard holds 64 of the 512
+    intermediate rows of every expert and of the shared expert, the router whole):
+    every shard routes the same way, and the eight partial outputs, summed as an
+    all-reduce would, give the whole layer's output within tolerance."""
+    dev = device()
+    shape, seed = synth.DECODE_BF16, 2
+    dl, lc = _decode_layer(shape, seed)
+    x = synth.make_tokens(shape, T, seed, stream=100 + T)
+    ref = orc.forward(oracle_layer(lc), oracle_tokens(x), nthreads=oracle_threads())
+    mf = _plan(shape, T, "fused")
+    full = run_gpu(mf, dl, x.to(dev))
+    mf.close()
+    total = torch.zeros_like(full["out"], dtype=torch.float64)
+    step = shape.inter // 8
+    for r in range(8):
+        print(f"[tp8] T={T} shard {r}", flush=True)
+        sh = _shard(dl, r * step, (r + 1) * step)
+        mf = _plan(sh["shape"], T, "fused")
+        got = run_gpu(mf, sh, x.to(dev))
+        mf.close()
+        assert torch.equal(got["ids"], full["ids"]), f"shard {r} routes differently"
+        total += got["out"].double()
+    scale = float(np.max(np.abs(ref["out"])))
+    err_sum = float(np.max(np.abs(total.numpy() - ref["out"])))
+    err_full = float(np.max(np.abs(full["out"].double().numpy() - ref["out"])))
+    print(f"  max |sum of shards - oracle| {err_sum:.3e}, max |layer - oracle| {err_full:.3e}, "
+          f"scale {scale:.3e}", flush=True)
+    assert err_sum <= TOL_LOWP * scale
 
 
 SPLIT_JOIN_CASES = {
