@@ -139,7 +139,7 @@ typedef struct moe_ffn_desc {
     int32_t weight_dtype;       /* moe_ffn_dtype of every routed and shared FFN matrix */
     uint32_t flags;             /* MOE_FFN_SHARED_*, MOE_FFN_FORCE_*, MOE_FFN_INPUT_NORM,
                                    MOE_FFN_RESIDUAL, MOE_FFN_DEBUG_* */
-    int32_t matvec_max_tokens;  /* regime switch; 0 = library default (6) */
+    int32_t matvec_max_tokens;  /* regime switch; 0 = library default (16) */
     float norm_eps;             /* INPUT_NORM epsilon (>= 0, finite); ignored otherwise */
 } moe_ffn_desc;
 
@@ -189,11 +189,12 @@ typedef struct moe_ffn_plan_info {
 
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
-    MOE_FFN_K_ROUTER = 0,       /* router GEMV (logits and the shared-gate logit); for batches of
-                                   33..256 tokens also the routing, in the same launch */
-    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) up to 32 tokens,
+    MOE_FFN_K_ROUTER = 0,       /* router (logits and the shared-gate logit): a GEMV up to 16 tokens
+                                   (and for fp32 tokens or with the input norm), an MFMA GEMM
+                                   above */
+    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) up to 16 tokens,
                                    except up to 4 tokens in the mat-vec regime, where the routed
-                                   gate/up launch routes; above 256 tokens the ranking launch
+                                   gate/up launch routes; above 16 tokens the ranking launch
                                    (top-k, renormalisation, per-expert counts) */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
@@ -203,7 +204,7 @@ typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_GG_GATE_UP = 7,   /* grouped MFMA gate/up (routed, or routed + shared when fused) */
     MOE_FFN_K_GG_DOWN = 8,      /* grouped MFMA down (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN_JOIN = 9,    /* mat-vec regime: down of every pair of a row tile + the join */
-    MOE_FFN_K_BUCKET = 10,      /* above 256 tokens: bucketing of the ranked pairs by expert (two
+    MOE_FFN_K_BUCKET = 10,      /* above 16 tokens: bucketing of the ranked pairs by expert (two
                                    launches: the per-expert scan of the counts, the placement) */
     MOE_FFN_K_COUNT = 11
 } moe_ffn_kernel_id;

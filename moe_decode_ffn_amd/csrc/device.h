@@ -107,26 +107,13 @@ __device__ __forceinline__ void bf16x8_to_q4_order(const uint32_t x[4], uint32_t
     out[3] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);  // (x5, x7)
 }
 
-// ---- cross-workgroup hand-off ----------------------------------------------------
-// All threads of the workgroup call it.  Publishes the workgroup's global
-// writes (every wave waits for its own stores, then one agent-scope release)
-// and counts the workgroup in; returns true in the n-th (last) arrival, which
-// resets the counter and acquires everything the others published.
-__device__ inline bool last_arrival(unsigned *ctr, unsigned n) {
-    __shared__ int s_last;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old + 1 == n;
-        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last ? 1 : 0;
-    }
-    __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return last;
+// Workgroup barrier ordering LDS accesses only: global loads and stores in flight
+// are not waited for, as they would be by __syncthreads (which waits for every
+// outstanding memory access of the wave before the barrier).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 }  // namespace moeffn

@@ -96,9 +96,6 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
         return hip_fail(e, "hipEventCreateWithFlags");
     if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "hipEventCreateWithFlags");
-    const size_t tb = kTicketCount * sizeof(unsigned);
-    if ((e = hipMalloc(&P->tickets, tb)) != hipSuccess) return hip_fail(e, "hipMalloc");
-    if ((e = hipMemsetAsync(P->tickets, 0, tb, stream)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
     if ((e = hipDeviceGetAttribute(&P->cu_count, hipDeviceAttributeMultiprocessorCount, P->d.device)) != hipSuccess)
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
@@ -228,9 +225,10 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.x_bf16 = d.x_dtype == MOE_FFN_BF16;
     rp.T = Ti; rp.H = (int)H; rp.E = (int)E;
     rp.router = t->w_router; rp.gate_vec = t->gate_vec; rp.logits = logits;
-    // tokens per router workgroup column: 4 for small batches, so that the last
-    // workgroup of each column ranks one token per wave; 8 above
-    rp.tok_tile = std::max(1, std::min(Ti <= 16 ? 4 : 8, (int)(kStageBytes / (H * xb))));
+    // tokens per router workgroup column: 4 up to 32 tokens (more workgroups), 8 above
+    // (the GEMV router serves up to 16 bf16 tokens, and fp32 tokens or the input norm at
+    // any batch)
+    rp.tok_tile = std::max(1, std::min(Ti <= 32 ? 4 : 8, (int)(kStageBytes / (H * xb))));
     const int r_rows = router_rows_per_wg(P->map_router);
     const int r_grid = (int)((E + 1 + r_rows - 1) / r_rows);
     const int r_tiles = (Ti + rp.tok_tile - 1) / rp.tok_tile;
@@ -240,7 +238,6 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.pairs = pairs; rp.pos_expert = pos_expert;
     rp.dbg_ids = t->dbg_topk_ids; rp.dbg_w = t->dbg_topk_weights;
     rp.dbg_logits = t->dbg_logits; rp.dbg_gate = t->dbg_shared_gate;
-    rp.tickets = P->tickets;
     rp.norm_w = t->norm_weight; rp.norm_eps = d.norm_eps; rp.xn = W + L.xn;
 
     GateUpParams gp{};
@@ -266,13 +263,12 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
                         gate_up_lds_bytes(q, (int)xb) <= kLdsLimit ? 1 : 0;
         gp.route_lds_off = gate_up_route_lds_off(q, (int)xb);
     }
-    // else a routing launch of its own (one wave per token) or the router's tail
+    // else a routing launch of its own (one wave per token, up to 16 tokens)
     const bool route_kernel = !gp.route_here && Ti <= kRouteKernelMax &&
                               route_kernel_lds_bytes(Ti, (int)k, (int)E) <= kLdsLimit;
-    // large batches (or a routing tail that does not fit in LDS): ranking and bucketing
-    // launches of their own, through global memory
-    const bool batch_route = Ti > kTailMaxTokens || (!gp.route_here && !route_kernel && !P->tail_ok);
-    rp.route_tail = gp.route_here || route_kernel || batch_route ? 0 : 1;
+    // larger batches (or a shape whose routing does not fit in LDS): ranking and
+    // bucketing launches of their own, through global memory
+    const bool batch_route = !gp.route_here && !route_kernel;
     rp.bcount = batch_route ? (int *)(W + L.bcount) : nullptr;
     const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
     gp.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
@@ -499,7 +495,6 @@ void moe_ffn_destroy(moe_ffn_plan_t P) {
     if (P->ev_fork) hipEventDestroy(P->ev_fork);
     if (P->ev_join) hipEventDestroy(P->ev_join);
     if (P->aux) hipStreamDestroy(P->aux);
-    if (P->tickets) hipFree(P->tickets);
     delete P;
 }
 

@@ -18,13 +18,10 @@ constexpr int kMaxTokens = 16384;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
-constexpr int kDefaultMatvecMax = 6;  // measured crossover of the mat-vec and grouped-GEMM kernels
+constexpr int kDefaultMatvecMax = 16;  // measured crossover of the mat-vec and grouped-GEMM kernels
 constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
-constexpr int kRouteKernelMax = 32;   // up to this batch k_route routes it (else the router tail)
-constexpr int kTailMaxTokens = 256;   // up to this batch the router tail routes it (else batch routing)
+constexpr int kRouteKernelMax = 16;   // up to this batch k_route routes it (else the batch launches)
 constexpr int kPfMinBucket = 32;      // mean tokens per used expert from which the prefill GEMM runs
-// arrival counters in plan memory: one per router token tile, one across tiles
-constexpr int kTicketCount = kTailMaxTokens + 1;
 constexpr size_t kWsAlign = 256;
 constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
 constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
@@ -85,13 +82,11 @@ struct moe_ffn_plan_s {
     bool ready = false;
     hipStream_t aux = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-    unsigned *tickets = nullptr;  // device arrival counters of the router's routing tail
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
     int occ_pf_gu[3] = {0, 0, 0}, occ_pf_d[3] = {0, 0, 0};  // prefill GEMM, 128/192/256 tokens per pass
     bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
-    bool tail_ok = true;    // the router's LDS routing tail fits for every batch up to kTailMaxTokens
     // profiling
     bool profiling = false;
     std::vector<moeffn::ProfRec> prof;
@@ -125,8 +120,6 @@ struct RouterParams {
     int *pos_expert;        // [T*k]
     int32_t *dbg_ids;
     float *dbg_w, *dbg_logits, *dbg_gate;
-    unsigned *tickets;      // plan memory: [kTailMaxTokens] per token tile + [1] across tiles, zero between calls
-    int route_tail;         // 1: the launch also ranks and buckets (else k_route or the gate/up launch)
     // input RMSNorm: logits from the normalised tokens; workgroup column 0 writes them for the experts
     const float *norm_w;    // [H] or NULL: no norm
     float norm_eps;
@@ -279,7 +272,6 @@ int down_rows_per_wg(int wkind, const RowMap &m);
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);
 int gate_up_route_lds_off(const GateUpParams &p, int xbytes);
 size_t router_lds_bytes(const RouterParams &p);
-size_t route_lds_bytes(int T, int k, int E);
 size_t route_kernel_lds_bytes(int T, int k, int E);
 hipError_t launch_route(const RouterParams &p, hipStream_t s);
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s);

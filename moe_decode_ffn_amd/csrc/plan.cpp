@@ -148,9 +148,9 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
     }
 
-    // the router's routing tail ranks and buckets up to kTailMaxTokens tokens in LDS; where
+    // the routing launch ranks and buckets up to kRouteKernelMax tokens in LDS; where
     // that does not fit (many experts and picks), those batches take batch routing too
-    P->tail_ok = route_lds_bytes(std::min(d.max_tokens, kTailMaxTokens), k, E) <= kLdsLimit;
+    const bool route_fits = route_kernel_lds_bytes(std::min(d.max_tokens, kRouteKernelMax), k, E) <= kLdsLimit;
 
     Layout &L = P->L;
     size_t c = 0;
@@ -167,8 +167,8 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.logits = c;     c += align_up(T * (E + 1) * 4);
     // normalised input of both branches (x_dtype), router -> experts
     L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
-    // batch routing's counts, prefixes and ranks (batches above kTailMaxTokens)
-    const bool batch_possible = d.max_tokens > kTailMaxTokens || !P->tail_ok;
+    // batch routing's counts, prefixes and ranks (batches above kRouteKernelMax)
+    const bool batch_possible = d.max_tokens > kRouteKernelMax || !route_fits;
     L.bcount = c;     c += batch_possible ? align_up(batch_route_ints(d.max_tokens, k, E) * 4) : 0;
     L.routing_bytes = c - L.shared_bytes;
     // sequential steps: gate/up holds h, down holds h and y, join holds y

@@ -41,14 +41,6 @@ __device__ __forceinline__ floatx4_t pf_mfma(uint4 a, uint4 b, floatx4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Workgroup barrier ordering LDS accesses only: global loads in flight (the stages
-// prefetched ahead) are not waited for, as they would be by __syncthreads.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 struct PfJob {
     bool valid, routed;
     const uint8_t *W0, *W1;  // gate/up: gate and up matrices; down: the matrix (W1 unused)

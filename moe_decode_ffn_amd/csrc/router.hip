@@ -1,18 +1,15 @@
-// router.hip -- router GEMV (fp32 rows; row E is the shared-expert gate
-// vector, so its logit is sigma's argument) with the routing folded into the
-// same launch.
+// router.hip -- the router (fp32 rows; row E is the shared-expert gate vector, so
+// its logit is sigma's argument) and the routing launches.
 //
-// Workgroups tile (rows x tokens).  Where the routing runs depends on the
-// batch: in every gate/up workgroup (a few tokens), in k_route (one wave per
-// token, mid-size batches), or in this launch's tail (larger batches): after
-// writing its logits a workgroup takes a ticket for its token tile; the last one to arrive for a tile ranks that
-// tile's tokens (one wave per token, routing.h): ids, renormalised weights and
-// the shared-expert gate.  With several token tiles a second ticket elects
-// the last tile, which buckets every (token, slot) pair by expert and writes
-// the tables the expert kernels read: one 64-byte job record per used expert
-// (expert, first position, count, 0, first 12 pair ids) so an expert
-// workgroup learns everything about its job from one scalar load.  Tickets are
-// counters in plan memory that the last arriver puts back to zero.
+// Logits: a GEMV over (rows x token tiles) for small batches, bf16 tokens with the
+// input norm or fp32 tokens; an MFMA GEMM over an exact bf16 split of the rows above
+// 16 bf16 tokens.  Where the routing runs depends on the batch: in every gate/up
+// workgroup (a few tokens), in k_route (one wave per token, up to 16 tokens), or in
+// the batch launches (ranking, a per-expert scan of the counts, placement).  Every
+// path writes the same tables: ids, renormalised weights and the shared-expert gate
+// per token, the pairs bucketed by expert, and one 64-byte job record per used
+// expert (expert, first position, count, 0, first 12 pair ids) so an expert
+// workgroup learns everything about its job from one scalar load.
 #include "device.h"
 #include "internal.h"
 #include "routing.h"
@@ -178,28 +175,10 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
             }
         }
     }
-
-    // ---- routing tail ----
-    if (!p.route_tail) return;
-    if (!last_arrival(p.tickets + blockIdx.y, gridDim.x)) return;
-    const int T = p.T, k = p.k;
-    const RouteLds L = route_lds_layout(T, k, E, false);
-    const bool one_tile = gridDim.y == 1;
-    const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
-                        p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
-    rank_tokens(p.logits, t0, t0 + nt, E, k, lds, L, g, !one_tile);
-    if (!one_tile) {
-        if (!last_arrival(p.tickets + kTailMaxTokens, gridDim.y)) return;
-        int *ids = reinterpret_cast<int *>(lds + L.ids);
-        for (int i = tid; i < T * k; i += blockDim.x) ids[i] = p.ids[i];
-    }
-    bucket_tokens(T, k, E, lds, L, g);
 }
 
-size_t route_lds_bytes(int T, int k, int E) { return route_lds_layout(T, k, E, false).bytes; }
-
 // k_route: one workgroup, one wave per token (up to 16), ranks the batch and
-// buckets it (mid-size batches, between in-gate/up routing and the router tail).
+// buckets it (5 to 16 tokens, and fewer where the gate/up workgroups cannot).
 __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     const RouteLds L = route_lds_layout(p.T, p.k, p.E, false);
@@ -209,13 +188,13 @@ __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
     bucket_tokens(p.T, p.k, p.E, lds, L, g);
 }
 
-// ---- router GEMM for large batches ------------------------------------------------------
+// ---- router GEMM for batches above 16 tokens ---------------------------------------------
 // logits[t][e] = sum_h W[e][h] x[t][h] on v_mfma_f32_16x16x32_bf16.  The tokens are bf16;
 // each fp32 router weight is split exactly into three bf16 pieces (hi = the top 16 bits,
 // mid = the top 16 bits of the rest, lo = what remains, at most 8 significant bits), so
 // every product piece * token is exact in fp32 and the three accumulate into one fp32
 // sum: the logits carry fp32-GEMV accuracy.  A wave owns 16 rows (experts, the gate
-// vector as row E) and 64 tokens; a workgroup 64 rows.  K in steps of 32; lane group g
+// vector as row E), 16 * NT tokens and a quarter of K.  K in steps of 32; lane group g
 // holds elements 8g..8g+7 of a step for both operands.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rfloatx4_t __attribute__((ext_vector_type(4)));
@@ -245,7 +224,6 @@ __device__ __forceinline__ void split3(const float4 &u, const float4 &v, uint4 &
     lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
 }
 
-constexpr int kRgRows = 64;    // rows per workgroup (16 per wave)
 
 // One K step (32 elements) of a wave: its 16 weight rows (8 fp32 per lane) and its
 // token tiles (8 bf16 per lane each).  Steps are loaded two ahead in three register
@@ -257,13 +235,18 @@ struct RgStep {
     uint4 b[NT];
 };
 
+// A workgroup owns 16 rows and 16 * NT tokens, and its four waves split K in quarters
+// (workgroups of 64 rows over the whole of K left most of the GPU idle below a few
+// thousand tokens and were slower at every size measured); the partial sums meet in
+// LDS and wave 0 adds them in wave order (((w0 + w1) + w2) + w3) and stores the logits.
 template <int NT>
 __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     constexpr int kRgTiles = NT, kRgTokens = 16 * NT;
+    __shared__ float s_part[3][kRgTiles][4][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = lane & 15, g = lane >> 4;
     const int H = p.H, E = p.E, T = p.T;
-    const int row = blockIdx.x * kRgRows + wave * 16 + ri;      // A row of this lane
+    const int row = blockIdx.x * 16 + ri;  // A row of this lane (rows past E read the gate vector)
     const float *W = (row < E ? p.router + (size_t)row * H : p.gate_vec) + 8 * g;
     const int t0 = blockIdx.y * kRgTokens;
     const uint16_t *xb[kRgTiles];
@@ -275,9 +258,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     rfloatx4_t acc[kRgTiles];
 #pragma unroll
     for (int n = 0; n < kRgTiles; ++n) acc[n] = rfloatx4_t{0.f, 0.f, 0.f, 0.f};
+    // this wave's steps: s0 .. s0 + per - 1 (H is a multiple of 128, so per >= 1); loads
+    // past the last step re-read the last one and are never used
+    const int per = H / 128, s0 = wave * per;
     RgStep<NT> st[3];
     auto load = [&](RgStep<NT> &d, int s) {
-        const int ko = 32 * s;
+        const int ko = 32 * (s0 + min(s, per - 1));
         d.wa = *reinterpret_cast<const float4 *>(W + ko);
         d.wb = *reinterpret_cast<const float4 *>(W + ko + 4);
 #pragma unroll
@@ -293,70 +279,85 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
             acc[n] = r_mfma(lo, d.b[n], acc[n]);
         }
     };
-    const int nstep = H / 32;  // a multiple of 4 (H is a multiple of 128 here)
     load(st[0], 0);
     load(st[1], 1);
     int s = 0;
-    for (; s + 4 < nstep; s += 3) {
+    for (; s + 4 < per; s += 3) {
         load(st[2], s + 2); mul(st[0]);
         load(st[0], s + 3); mul(st[1]);
         load(st[1], s + 4); mul(st[2]);
     }
-    // tail: at most four steps, sets continuing from s % 3 == 0
-    if (s + 2 < nstep) load(st[2], s + 2);
+    if (s + 2 < per) load(st[2], s + 2);
     mul(st[0]);
-    if (s + 1 < nstep) { if (s + 3 < nstep) load(st[0], s + 3); mul(st[1]); }
-    if (s + 2 < nstep) mul(st[2]);
-    if (s + 3 < nstep) mul(st[0]);
-    // lane holds rows 4g + v of the wave's 16 for token column ri
+    if (s + 1 < per) { if (s + 3 < per) load(st[0], s + 3); mul(st[1]); }
+    if (s + 2 < per) mul(st[2]);
+    if (s + 3 < per) mul(st[0]);
+    if (wave > 0) {
+#pragma unroll
+        for (int n = 0; n < kRgTiles; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s_part[wave - 1][n][v][lane] = acc[n][v];
+    }
+    lds_barrier();
+    if (wave != 0) return;
+    // lane holds rows 4g + v of the workgroup's 16 for token column ri
 #pragma unroll
     for (int n = 0; n < kRgTiles; ++n) {
         const int t = t0 + 16 * n + ri;
         if (t >= T) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int e = blockIdx.x * kRgRows + wave * 16 + 4 * g + v;
-            if (e <= E) p.logits[(size_t)t * (E + 1) + e] = acc[n][v];
+            const int e = blockIdx.x * 16 + 4 * g + v;
+            const float sum = ((acc[n][v] + s_part[0][n][v][lane]) + s_part[1][n][v][lane]) + s_part[2][n][v][lane];
+            if (e <= E) p.logits[(size_t)t * (E + 1) + e] = sum;
         }
     }
 }
 
 hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s) {
     if (!p.x_bf16 || p.norm_w || p.H % 128 != 0) return hipErrorInvalidValue;
-    // wider token blocks for big batches: fewer re-reads (and splits) of the weights
-    const int nt = p.T >= 4096 ? 4 : 2;
-    const dim3 grid((p.E + 1 + kRgRows - 1) / kRgRows, (p.T + 16 * nt - 1) / (16 * nt));
-    if (nt == 4) launch_kernel(k_router_mfma<4>, grid, dim3(256), 0, s, p);
-    else launch_kernel(k_router_mfma<2>, grid, dim3(256), 0, s, p);
+    // one 16-token tile per workgroup up to 256 tokens; wider token blocks above (fewer
+    // re-reads and splits of the rows)
+    const int nt = p.T <= 256 ? 1 : p.T < 4096 ? 2 : 4;
+    const dim3 grid((p.E + 1 + 15) / 16, (p.T + 16 * nt - 1) / (16 * nt));
+    if (nt == 1) launch_kernel(k_router_mfma<1>, grid, dim3(256), 0, s, p);
+    else if (nt == 2) launch_kernel(k_router_mfma<2>, grid, dim3(256), 0, s, p);
+    else launch_kernel(k_router_mfma<4>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 // ---- batch routing (large batches) ----------------------------------------------------
 // Three launches, no atomics, a deterministic result: buckets hold their pairs in pair
 // order, as the one-workgroup bucketing of smaller batches does.
-//   k_rank_batch    a workgroup ranks kRankTokensPerWg tokens (one wave per token in
-//                   turn), writes its row of per-expert counts and, per pair, the
+//   k_rank_batch    a workgroup ranks a group of tokens (one wave per token in turn),
+//                   writes its row of per-expert counts and, per pair, the
 //                   number of earlier pairs of the workgroup with the same expert;
 //   k_count_scan    per expert, the exclusive prefix of the count rows (in place) and
 //                   the expert's total;
 //   k_bucket_batch  every workgroup scans the totals (expert offsets, used-expert
 //                   slots); workgroup 0 writes the job records; each pair goes to
 //                   offset + prefix of its workgroup + its rank inside the workgroup.
-// bcount layout (ints): totals [E], then the count rows [W][E] (W = ceil(T / 16)),
-// then the in-workgroup ranks [T*k].
-constexpr int kRankTokensPerWave = 4;
-constexpr int kRankTokensPerWg = 4 * kRankTokensPerWave;
-constexpr int kRankPairsMax = kRankTokensPerWg * kMaxTopK;
+// A ranking workgroup takes 4 tokens (one per wave) up to 4096 tokens and 16 (four per
+// wave in turn) above, where more count rows would cost the scan more than the
+// parallel ranking saves.
+// bcount layout (ints): totals [E], then the count rows [W][E] (W = ceil(T / tokens per
+// ranking workgroup)), then the in-workgroup ranks [T*k].
+constexpr int kRankTokensPerWaveMax = 4;
+constexpr int kRankPairsMax = 4 * kRankTokensPerWaveMax * kMaxTopK;
+
+static __host__ __device__ int rank_tokens_per_wave(int T) { return T > 4096 ? 4 : 1; }
+static __host__ __device__ int rank_tokens_per_wg(int T) { return 4 * rank_tokens_per_wave(T); }
 
 __global__ __launch_bounds__(256) void k_rank_batch(RouterParams p) {
     __shared__ int s_ids[kRankPairsMax];
     __shared__ int s_hist[kMaxExperts];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = p.E, k = p.k;
-    const int tw0 = blockIdx.x * kRankTokensPerWg;
-    const int ntw = min(kRankTokensPerWg, p.T - tw0);
+    const int tpw = rank_tokens_per_wave(p.T);
+    const int tw0 = blockIdx.x * 4 * tpw;
+    const int ntw = min(4 * tpw, p.T - tw0);
     for (int e = tid; e < E; e += 256) s_hist[e] = 0;
-    for (int i = 0; i < kRankTokensPerWave; ++i) {
+    for (int i = 0; i < tpw; ++i) {
         const int lt = i * 4 + wave, t = tw0 + lt;
         if (lt >= ntw) break;
         RouteOut o{p.ids + (size_t)t * k, p.wts + (size_t)t * k, p.gate_s + t,
@@ -417,7 +418,8 @@ __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
     const int E = p.E, NP = p.T * p.k, k = p.k;
     const int *cnt = p.bcount;
     const int *pre = p.bcount + E;
-    const int W = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    const int tpg = rank_tokens_per_wg(p.T);
+    const int W = (p.T + tpg - 1) / tpg;
     const int *rank = p.bcount + E + (size_t)W * E;
     // exclusive scans of cnt[] and (cnt[] > 0): thread owns two consecutive experts
     const int e0 = 2 * tid;
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
     for (int q = blockIdx.x * kBucketPairsPerWg + tid; q < q_end; q += 256) {
         const int e = p.ids[q];
         if (e < 0 || e >= E) continue;
-        const int w = (q / k) / kRankTokensPerWg;
+        const int w = (q / k) / tpg;
         const int r = pre[(size_t)w * E + e] + rank[q];  // place inside the expert's bucket
         const int pos = s_off[e] + r;
         if (r >= cnt[e] || pos >= NP) continue;  // only with corrupt counts
@@ -461,19 +463,20 @@ __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
 }
 
 size_t batch_route_ints(int T, int k, int E) {
-    const size_t W = (T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    // the most count rows any batch up to T tokens needs
+    const size_t W = T > 4096 ? std::max<size_t>(1024, ((size_t)T + 15) / 16) : ((size_t)T + 3) / 4;
     return (size_t)E + W * E + (size_t)T * k;
 }
 
 hipError_t launch_rank_batch(const RouterParams &p, hipStream_t s) {
-    const int grid = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    const int grid = (p.T + rank_tokens_per_wg(p.T) - 1) / rank_tokens_per_wg(p.T);
     if (p.k > kMaxTopK || p.E > kMaxExperts) return hipErrorInvalidValue;
     launch_kernel(k_rank_batch, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_count_scan(const RouterParams &p, hipStream_t s) {
-    const int W = (p.T + kRankTokensPerWg - 1) / kRankTokensPerWg;
+    const int W = (p.T + rank_tokens_per_wg(p.T) - 1) / rank_tokens_per_wg(p.T);
     launch_kernel(k_count_scan, dim3(p.E), dim3(256), 0, s, p, W);
     return hipGetLastError();
 }
@@ -499,9 +502,7 @@ hipError_t launch_route(const RouterParams &p, hipStream_t s) {
 }
 
 size_t router_lds_bytes(const RouterParams &p) {
-    const size_t stage = (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
-    const size_t tail = p.route_tail ? route_lds_bytes(p.T, p.k, p.E) : 0;
-    return stage > tail ? stage : tail;
+    return (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
 }
 
 template <int LPR, int NC>

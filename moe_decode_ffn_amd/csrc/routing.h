@@ -1,6 +1,6 @@
 // routing.h -- top-k ranking of one token by one wave, and bucketing of the
-// (token, slot) pairs by expert inside one workgroup (the router launch's
-// routing tail).
+// (token, slot) pairs by expert inside one workgroup (the routing launch, or
+// every gate/up workgroup of a batch of a few tokens).
 //
 // Ranking: experts ordered by (logit descending, index ascending); ids are the
 // first k in that order; p = softmax over all experts; w_j = p_j / sum_j p_j.
@@ -28,75 +28,89 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Largest key over the wave, in every lane: a max butterfly inside each row of
-// 16 lanes (DPP), then the four row maxima read as scalars.
-__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+// Largest / smallest value over the wave, in every lane, in vector registers only
+// (no round trip through scalar registers): a butterfly inside each row of 16 lanes
+// (DPP), then the rows combined by swapping the two halves of the wave and then
+// neighbouring rows (gfx950 permlane swaps), taking the max (min) of each lane's
+// value and the swapped one.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xf, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xf, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xf, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xf, 0xf, false));
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(a, b), max(c, d));
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max((uint32_t)a[0], (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xf, 0xf, false));
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = min((uint32_t)a[0], (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return min((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// The logit of a key (the inverse of logit_key; a -0 logit comes back as +0, which
+// gives the same weights).
+__device__ __forceinline__ float key_logit(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 // One wave ranks one token.  lg: E+1 logits (column E = shared-gate logit).
 // Expert e = lane * EPL + i sits in register slot i of its lane.  The k picks
 // are taken one per round in rank order: the largest remaining key over the
-// wave; among equal keys the lowest lane, and in it the lowest slot, which is
-// the lowest expert index.  The winner drops the pick and lane r keeps pick r.
-// Keys of real logits are at least 1 (0 marks a taken or padding slot), so the
-// picks are k distinct experts whatever the logits hold.
+// wave, and among equal keys the lowest expert index (the smallest index of a
+// slot holding that key, over the wave); the pick's slot is cleared and lane r
+// keeps pick r.  Keys of real logits are at least 1 (0 marks a taken or
+// padding slot), so the picks are k distinct experts whatever the logits hold.
+// A round is a chain of dependent vector instructions (its cost is their issue
+// latency, ~7 cycles each for one wave).
 // Weights: p_e = exp(l_e - max l) / sum_all exp(.) renormalised over the picks
 // is w_j = exp(l_j - m) / sum_picks exp(l_i - m) for any m (the full sum
 // cancels); m = the first pick, the largest logit.
 template <int EPL>
 __device__ void route_token(const float *lg, int E, int k, int lane, const RouteOut &o) {
-    float v[EPL];
     uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
-        v[i] = e < E ? lg[e] : -INFINITY;
-        key[i] = e < E ? max(logit_key(v[i]), 1u) : 0u;
+        key[i] = e < E ? max(logit_key(lg[e]), 1u) : 0u;
     }
     const float glog = lg[E];
     uint32_t best = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) best = max(best, key[i]);
 
-    int my_id = 0;
-    float my_v = 0.f;
+    uint32_t my_id = 0, my_key = 0;
     for (int r = 0; r < k; ++r) {
-        const uint32_t M = wave_max_key(best);
-        const int win = (int)__builtin_ctzll(__ballot(best == M));
-        int wi = 0;
-        float wv = v[0];
+        const uint32_t M = wave_max_u32(best);
+        uint32_t cand = 0xffffffffu;
 #pragma unroll
         for (int i = EPL - 1; i >= 0; --i)
-            if (key[i] == M) { wi = i; wv = v[i]; }
-        const int slot = __builtin_amdgcn_readlane(wi, win);
-        const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), win));
-        if (lane == win) {
-            best = 0u;
+            if (key[i] == M) cand = (uint32_t)(lane * EPL + i);
+        const uint32_t win = wave_min_u32(cand);
+        best = 0u;
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                if (i == slot) key[i] = 0u;
-                best = max(best, key[i]);
-            }
+        for (int i = 0; i < EPL; ++i) {
+            if ((uint32_t)(lane * EPL + i) == win) key[i] = 0u;
+            best = max(best, key[i]);
         }
-        if (lane == r) { my_id = win * EPL + slot; my_v = val; }
+        if (lane == r) { my_id = win; my_key = M; }
     }
+    const float my_v = key_logit(my_key);
     const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     const float myp = lane < k ? expf(my_v - m) : 0.f;
     const float psum = seg_sum<64>(myp);
     if (lane < k) {
         const float w = myp / psum;
-        o.ids[lane] = my_id;
+        o.ids[lane] = (int)my_id;
         o.w[lane] = w;
-        if (o.dbg_ids) o.dbg_ids[lane] = my_id;
+        if (o.dbg_ids) o.dbg_ids[lane] = (int)my_id;
         if (o.dbg_w) o.dbg_w[lane] = w;
     }
     if (lane == 0) {
@@ -169,7 +183,8 @@ __device__ inline void bucket_pairs_wave(const int *ids, int NP, int E, int4 *sl
 }
 
 // Bucketing of all T*k pairs by one workgroup (any multiple of 64 threads up
-// to 1024).  ids[] may be in LDS or global memory.  Outputs (any memory):
+// to 1024).  ids[], the scratch and the outputs are in LDS (the barriers
+// inside order LDS accesses only).  Outputs:
 // slots[u] = (expert, first position, count, 0) for used experts in ascending
 // order, pairs[pos] = t*k + j, pos_expert[pos], *n_unique.  Positions are
 // expert-major, tokens ascending within an expert; a token's rank in its
@@ -185,18 +200,18 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
     int *off = cnt + E;                           // [E] first position of expert e
     int *wtot = off + E;                          // [2 * 16] wave totals
     for (int i = tid; i < E * W; i += nth) mask[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int q = tid; q < NP; q += nth) {
         const int t = q / k, e = ids[q];
         if (e >= 0 && e < E) atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += nth) {
         int c = 0;
         for (int w = 0; w < W; ++w) c += __popc(mask[e * W + w]);
         cnt[e] = c;
     }
-    __syncthreads();
+    lds_barrier();
     // exclusive scans of cnt[] and (cnt[] > 0); thread owns EPT consecutive experts
     const int EPT = (E + nth - 1) / nth;
     int a = 0, b = 0;
@@ -210,7 +225,7 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
         if (lane >= d) { ia += ya; ib += yb; }
     }
     if (lane == 63) { wtot[wave] = ia; wtot[16 + wave] = ib; }
-    __syncthreads();
+    lds_barrier();
     int ba = ia - a, bb = ib - b;
     for (int w = 0; w < wave; ++w) { ba += wtot[w]; bb += wtot[16 + w]; }
     for (int i = 0; i < EPT; ++i) {
@@ -227,7 +242,7 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
         for (int w = 0; w < nw; ++w) nu += wtot[16 + w];
         *n_unique = nu;
     }
-    __syncthreads();
+    lds_barrier();
     for (int q = tid; q < NP; q += nth) {
         const int t = q / k, e = ids[q];
         if (e < 0 || e >= E) continue;
@@ -316,7 +331,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
     int *nup = reinterpret_cast<int *>(area + L.nu);
     int4 *slots = reinterpret_cast<int4 *>(area + L.slots);
     int *rec = reinterpret_cast<int *>(area + L.records);
-    __syncthreads();
+    lds_barrier();
     if (T == 1) {  // one token: its k picks are k distinct experts, one bucket each, in rank order
         if (threadIdx.x < 64) {
             const int j = threadIdx.x;
@@ -333,7 +348,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
     } else {
         bucket_pairs(ids, T, k, E, reinterpret_cast<uint32_t *>(area + L.scratch), slots, pairs, pose, nup);
     }
-    __syncthreads();
+    lds_barrier();
     const int nu = *nup;
     for (int i = tid; i < nu * kRecInts; i += blockDim.x) {
         const int u = i / kRecInts, f = i - u * kRecInts;
@@ -354,7 +369,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
             g.pos_expert[i] = pose[i];
         }
     if (g.n_unique && tid == 0) *g.n_unique = nu;
-    __syncthreads();
+    lds_barrier();
     return nu;
 }
 

@@ -119,6 +119,17 @@ def _align(v):
     return (v + 255) // 256 * 256
 
 
+def _batch_routing_ints(T, k, E):
+    """Above 16 tokens the batch is ranked and bucketed by launches of their own,
+    through global memory: per-expert totals, one count row per ranking workgroup
+    (4 tokens up to 4096 tokens, 16 above: room for the most rows any batch up to
+    T needs) and each pair's rank inside its workgroup."""
+    if T <= 16:
+        return 0
+    W = max(1024, (T + 15) // 16) if T > 4096 else (T + 3) // 4
+    return E + W * E + T * k
+
+
 @pytest.mark.parametrize("T", [1, 8, 64, 128])
 def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     H, E, k, I, Is = 2048, 256, 8, 512, 512
@@ -127,9 +138,10 @@ def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     ffn.moe_ffn_destroy(plan)
     shared = _align(T * Is * 4) + _align(T * H * 4)
     # routing region: gate, ids, weights, one 64-byte job record per expert, used-expert
-    # count, bucketed pairs and their experts, logits [T][E+1]
+    # count, bucketed pairs and their experts, logits [T][E+1], batch routing's ints
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
                + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4))
+    routing += _align(_batch_routing_ints(T, k, E) * 4) if T > 16 else 0
     h, y = _align(T * k * I * 4), _align(T * k * H * 4)
     phases = {"gate/up": h, "down": h + y, "join": y}  # live scratch of each sequential step
     assert info.shared_region_bytes == shared
@@ -168,34 +180,29 @@ def test_plan_rejects_bad_norm_eps(lib, eps):
     ffn.moe_ffn_destroy(p)
 
 
-@pytest.mark.parametrize("T", [257, 4096])
+@pytest.mark.parametrize("T", [257, 4096, 8192])
 def test_workspace_with_batch_routing(lib, T):
-    # above 256 tokens the routing region also holds the bucketing launches' ints:
-    # per-expert totals, one count row per ranking workgroup of 16 tokens, and each
-    # pair's rank inside its workgroup
+    # above 16 tokens the routing region also holds the bucketing launches' ints
     H, E, k, I, Is = 2048, 256, 8, 512, 512
     plan, ws = ffn.moe_ffn_plan(desc(max_tokens=T))
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
-    W = (T + 15) // 16
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align((E + W * E + T * k) * 4))
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
     assert info.routing_region_bytes == routing
     assert ws == info.workspace_bytes == (_align(T * Is * 4) + _align(T * H * 4) + routing
                                           + _align(T * k * I * 4) + _align(T * k * H * 4))
 
 
-def test_plan_with_no_room_for_the_lds_routing_tail(lib):
-    # 512 experts x top-32 at 256 tokens: the router's LDS routing tail would not fit, so
-    # the plan reserves batch routing's ints instead of refusing the shape
+def test_plan_with_the_largest_expert_count_and_top_k(lib):
+    # 512 experts x top-32 at 256 tokens: batch routing's ints for 8192 pairs
     E, k, T = 512, 32, 256
     plan, ws = ffn.moe_ffn_plan(desc(hidden=128, n_experts=E, top_k=k, inter=128, shared_inter=128,
                                      max_tokens=T))
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
-    W = (T + 15) // 16
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align((E + W * E + T * k) * 4))
+               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
     assert info.routing_region_bytes == routing
 
 
@@ -203,9 +210,9 @@ def test_auto_mode_defaults(lib):
     plan, _ = ffn.moe_ffn_plan(desc())
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
-    # measured on MI355X: mat-vec kernels win up to 6 tokens, the grouped GEMM above;
+    # measured on MI355X: mat-vec kernels win up to 16 tokens, the grouped GEMM above;
     # folding the shared expert into the routed launches wins in both regimes
-    assert info.matvec_max_tokens == 6
+    assert info.matvec_max_tokens == 16
     assert info.shared_mode_matvec == ffn.SHARED_FUSED
     assert info.shared_mode_gemm == ffn.SHARED_FUSED
     for m in (ffn.SHARED_AUX, ffn.SHARED_SEQ, ffn.SHARED_FUSED):

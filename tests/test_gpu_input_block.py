@@ -59,8 +59,8 @@ def test_small_layers(orc, name, block):
 
 
 FULL = {
-    # name: (shape, seed, tokens): routing in the gate/up launch (1), the grouped GEMM
-    # with its own routing launch (8), the router's routing tail (33), 4-bit (4)
+    # name: (shape, seed, tokens): routing in the gate/up launch (1), the routing
+    # launch (8), the grouped GEMM with the batch routing launches (33), 4-bit (4)
     "decode_bf16_t1": (synth.DECODE_BF16, 1, 1),
     "decode_bf16_t8": (synth.DECODE_BF16, 2, 8),
     "decode_bf16_t33": (synth.DECODE_BF16, 2, 33),

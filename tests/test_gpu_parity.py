@@ -113,16 +113,17 @@ def _decode_layer(shape, seed):
 
 FULL = {
     # name: (shape, seed, tokens, regime flags); the default regime switches to the
-    # grouped GEMM above 6 tokens for bf16, so the mat-vec kernels are also forced
-    # at batches beyond it; routing runs in the gate/up launch up to 4 tokens, in
-    # its own launch up to 32 and in the router's tail above
+    # grouped GEMM above 16 tokens for bf16, so both regimes are also forced at
+    # batches on the other side of it; routing runs in the gate/up launch up to 4
+    # tokens, in its own launch up to 16 and in the batch launches above
     "decode_bf16_t1": (synth.DECODE_BF16, 1, 1, 0),
     "decode_bf16_t4": (synth.DECODE_BF16, 2, 4, 0),
     "decode_bf16_t5": (synth.DECODE_BF16, 2, 5, 0),
     "decode_bf16_t7": (synth.DECODE_BF16, 2, 7, 0),
     "decode_bf16_t8": (synth.DECODE_BF16, 2, 8, 0),
-    "decode_bf16_t8_matvec": (synth.DECODE_BF16, 2, 8, ffn.FORCE_MATVEC),
-    "decode_bf16_t16_matvec": (synth.DECODE_BF16, 2, 16, ffn.FORCE_MATVEC),
+    "decode_bf16_t8_gemm": (synth.DECODE_BF16, 2, 8, ffn.FORCE_GEMM),
+    "decode_bf16_t16": (synth.DECODE_BF16, 2, 16, 0),
+    "decode_bf16_t17": (synth.DECODE_BF16, 2, 17, 0),
     "decode_bf16_t33": (synth.DECODE_BF16, 2, 33, 0),
     "decode_q4_t1": (synth.DECODE_Q4, 3, 1, 0),
     "decode_q4_t4": (synth.DECODE_Q4, 3, 4, 0),

@@ -1,4 +1,4 @@
-"""GPU parity of large batches (prefill): above 256 tokens the batch is ranked by
+"""GPU parity of large batches (prefill): above 16 tokens the batch is ranked by
 its own launch (one wave per token, per-workgroup expert counts), the counts are
 scanned per expert, and a third launch places every pair in its expert's bucket
 (offset + the prefix of its workgroup + its rank inside it), through global memory.
@@ -32,8 +32,7 @@ SMALL = {
     "bf16_gemm_matvec_forced": (synth.LayerShape(256, 12, 3, 128, 256, "bf16", "bf16"), 45, (300,),
                                 ffn.FORCE_MATVEC),
     # the largest expert count and top-k: 512 experts (two per scanning thread), 32 picks a
-    # token (512 pairs per ranking workgroup); with room for 300 tokens the router's LDS
-    # routing tail does not fit, so 100 tokens take batch routing too (20: the routing launch)
+    # token (128 pairs per ranking workgroup), 20 to 300 tokens: the batch launches
     "bf16_e512_k32": (synth.LayerShape(128, 512, 32, 128, 128, "bf16", "bf16"), 49, (20, 100, 300), 0),
 }
 
@@ -142,16 +141,18 @@ def test_repeated_runs_give_the_same_bits():
     mf.close()
 
 
-def test_router_logits_have_fp32_accuracy(orc):
-    """Above 256 tokens the router is an MFMA GEMM over an exact three-way bf16 split
-    of the fp32 weights: its logits must be as close to the fp64 oracle as an fp32
-    dot product (a plain bf16 rounding of the weights would be off by ~1e-3)."""
+@pytest.mark.parametrize("T", [17, 512, 4096])
+def test_router_logits_have_fp32_accuracy(orc, T):
+    """Above 16 tokens the router is an MFMA GEMM over an exact three-way bf16 split
+    of the fp32 weights (one, two or four 16-token tiles per workgroup by the batch):
+    its logits must be as close to the fp64 oracle as an fp32 dot product (a plain
+    bf16 rounding of the weights would be off by ~1e-3)."""
     dev = device()
-    shape, seed, T = synth.DECODE_BF16, 8, 512
+    shape, seed = synth.DECODE_BF16, 8
     dl = synth.make_layer_device(shape, seed, dev)
     lc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dl.items()}
     x = synth.make_tokens(shape, T, seed)
-    idx = np.arange(0, T, 16)
+    idx = np.arange(0, T, max(1, T // 32))
     mf = ffn.MoeFfn.for_shape(shape, max_tokens=T)
     got = run_gpu(mf, dl, x.to(dev))
     ref = orc.forward(oracle_layer(lc), oracle_tokens(x[torch.from_numpy(idx)]), nthreads=oracle_threads())
