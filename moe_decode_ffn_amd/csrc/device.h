@@ -33,9 +33,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 
 // ---- cross-lane ---------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
-// row_half_mirror (reverse within 8 lanes), row_mirror (reverse within 16).
+// quad_perm [3,2,1,0] (lane ^ 3), row_half_mirror (reverse within 8 lanes),
+// row_mirror (reverse within 16).
 constexpr int kDppXor1 = 0xb1;
 constexpr int kDppXor2 = 0x4e;
+constexpr int kDppRevQuad = 0x1b;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
@@ -46,7 +48,10 @@ __device__ __forceinline__ float dpp_f(float v) {
 
 // Sum over aligned segments of LPR lanes (LPR in 8, 16, 32, 64); the result is
 // in every lane of the segment.  Each step adds a lane's value to its partner's
-// (a + b in one lane, b + a in the other), so all lanes hold identical bits.
+// (a + b in one lane, b + a in the other), so all lanes hold identical bits.  The
+// steps across rows of 16 lanes use the gfx950 permlane swaps (no LDS round trip):
+// after a swap of a register with itself, one copy holds the lower partner's value
+// and the other the upper partner's in both lanes of every pair.
 template <int LPR>
 __device__ __forceinline__ float seg_sum(float v) {
     static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment size");
@@ -54,18 +59,14 @@ __device__ __forceinline__ float seg_sum(float v) {
     v = v + dpp_f<kDppXor2>(v);
     v = v + dpp_f<kDppHalfMirror>(v);
     if constexpr (LPR >= 16) v = v + dpp_f<kDppMirror>(v);
-    if constexpr (LPR >= 32) v = v + __shfl_xor(v, 16);
-    if constexpr (LPR >= 64) v = v + __shfl_xor(v, 32);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f<kDppXor1>(v));
-    v = fmaxf(v, dpp_f<kDppXor2>(v));
-    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_f<kDppMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
+    if constexpr (LPR >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    if constexpr (LPR >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
     return v;
 }
 
@@ -76,6 +77,19 @@ __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf
 // ---- 16-byte chunk loads ---------------------------------------------------------
 __device__ __forceinline__ uint4 ld16(const void *p) {
     return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Chunk loads of a 256-thread staging pass: thread tid takes chunks tid + 256q
+// (q < MAXC, below n), every load issued before any is used, so a pass costs one
+// memory round trip, not one per chunk (a plain loop waits for each load before
+// the next).  src(i) gives chunk i's address; a chunk at or past n reads as zero.
+template <int MAXC, typename Src>
+__device__ __forceinline__ void load_chunks(uint4 (&v)[MAXC], int n, int tid, Src src) {
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+        const int i = tid + 256 * q;
+        v[q] = i < n ? ld16(src(i)) : make_uint4(0, 0, 0, 0);
+    }
 }
 
 // ---- 4-bit blocks ------------------------------------------------------------------

@@ -225,12 +225,9 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     rp.x_bf16 = d.x_dtype == MOE_FFN_BF16;
     rp.T = Ti; rp.H = (int)H; rp.E = (int)E;
     rp.router = t->w_router; rp.gate_vec = t->gate_vec; rp.logits = logits;
-    // tokens per router workgroup column: 4 up to 32 tokens (more workgroups), 8 above
-    // (the GEMV router serves up to 16 bf16 tokens, and fp32 tokens or the input norm at
-    // any batch)
-    rp.tok_tile = std::max(1, std::min(Ti <= 32 ? 4 : 8, (int)(kStageBytes / (H * xb))));
-    const int r_rows = router_rows_per_wg(P->map_router);
-    const int r_grid = (int)((E + 1 + r_rows - 1) / r_rows);
+    // tokens per router workgroup: up to 8 (the GEMV router serves up to 16 bf16 tokens,
+    // and fp32 tokens or the input norm at any batch; one workgroup per row and tile)
+    rp.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / (H * xb))));
     const int r_tiles = (Ti + rp.tok_tile - 1) / rp.tok_tile;
 
     rp.k = (int)k;
@@ -244,6 +241,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gp.x = xe; gp.T = Ti; gp.H = (int)H; gp.k = (int)k; gp.E = (int)E;
     gp.x_resident = (size_t)Ti * H * xb <= kStageBytes ? 1 : 0;
     gp.tok_per_pass = std::max(1, (int)(kStageBytes / (H * xb)));
+    gp.x_sums = wk == W_Q4 ? 1 : 0;
     gp.wg = (const uint8_t *)t->w_gate; gp.wu = (const uint8_t *)t->w_up;
     gp.sg = t->w_gate_scale; gp.su = t->w_up_scale; gp.I = (int)I;
     gp.records = records; gp.n_unique = n_unique; gp.pairs = pairs; gp.h = h;
@@ -328,7 +326,7 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     const bool router_mfma = batch_route && rp.x_bf16 && !norm && H % 128 == 0;
     auto run_router = [&](hipStream_t s) {
         hipError_t e1 = timed(P, MOE_FFN_K_ROUTER, s, [&] {
-            return router_mfma ? launch_router_mfma(rp, s) : launch_router(rp, P->map_router, r_grid, r_tiles, s);
+            return router_mfma ? launch_router_mfma(rp, s) : launch_router(rp, r_tiles, s);
         });
         if (e1 != hipSuccess) return e1;
         if (route_kernel) return timed(P, MOE_FFN_K_ROUTE, s, [&] { return launch_route(rp, s); });

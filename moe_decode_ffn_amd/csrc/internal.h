@@ -19,12 +19,17 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
 constexpr int kDefaultMatvecMax = 16;  // measured crossover of the mat-vec and grouped-GEMM kernels
-constexpr int kRouteInGateUpMax = 4;  // up to this batch the gate/up workgroups route it themselves
+constexpr int kRouteInGateUpMax = 8;  // up to this batch the gate/up workgroups route it themselves
 constexpr int kRouteKernelMax = 16;   // up to this batch k_route routes it (else the batch launches)
 constexpr int kPfMinBucket = 32;      // mean tokens per used expert from which the prefill GEMM runs
 constexpr size_t kWsAlign = 256;
 constexpr size_t kLdsLimit = 64 * 1024;   // dynamic LDS per workgroup used by any kernel
 constexpr size_t kStageBytes = 32 * 1024; // activation staging per workgroup
+
+// Floats per token row of the logits table: E router logits, the shared-gate logit
+// at column E, padded to a multiple of 4 so that each row starts 16-byte aligned and
+// a lane reads four logits with one load.
+__host__ __device__ constexpr int logit_stride(int E) { return (E + 1 + 3) / 4 * 4; }
 
 // weight storage as the kernels see it
 enum WKind : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
@@ -77,7 +82,7 @@ struct moe_ffn_plan_s {
     uint32_t mode_gemm = MOE_FFN_SHARED_SEQ;
     int wkind = 0;
     // row maps: router rows (fp32, K=H), gate/up rows (K=H), down rows (K=max(I,Is))
-    moeffn::RowMap map_router, map_gu, map_down;
+    moeffn::RowMap map_gu, map_down;
     // lazily created device state
     bool ready = false;
     hipStream_t aux = nullptr;
@@ -134,6 +139,8 @@ struct GateUpParams {
     int T, H, k, E;
     int x_resident;                // 1: all T tokens staged in LDS once
     int tok_per_pass;              // else: tokens staged per pass
+    int x_sums;                    // 1 (4-bit weights): the stage also holds each 32-element
+                                   // block's sum of activations, after the tokens
     // routed experts
     const uint8_t *wg, *wu;        // [E][I] rows
     const uint16_t *sg, *su;       // Q4 scales [E][I][H/32]
@@ -251,8 +258,8 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream
 }
 
 // ---- launchers (kernel files) -------------------------------------------
-hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
-                         hipStream_t s);
+hipError_t launch_router(const RouterParams &p, int grid_tiles, hipStream_t s);
+int router_chunks_per_lane(int H);
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_down(const DownParams &p, int wkind, const RowMap &m, int grid, hipStream_t s);
 hipError_t launch_join(const JoinParams &p, hipStream_t s);
@@ -266,7 +273,6 @@ int gg_rows_per_job();
 hipError_t launch_delay(hipStream_t s, uint64_t ticks);
 
 // rows each workgroup covers for a kernel family and row map
-int router_rows_per_wg(const RowMap &m);
 int gate_up_rows_per_wg(int wkind, const RowMap &m);
 int down_rows_per_wg(int wkind, const RowMap &m);
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);

@@ -198,7 +198,7 @@ __device__ __forceinline__ void load_rows(const Job &jb, int wave, int seg, int 
 
 // ---- gate/up ------------------------------------------------------------------------------
 template <int WK, int LPR, int NC, int RPW>
-__device__ __forceinline__ void gate_up_token(const uint8_t *xr, int n_chunks, int sl,
+__device__ __forceinline__ void gate_up_token(const uint8_t *xr, const float *xbr, int n_chunks, int sl,
                                               const uint4 (&wg)[RPW][NC], const uint4 (&wu)[RPW][NC],
                                               const float (&sg)[RPW][NC], const float (&su)[RPW][NC],
                                               float (&g)[RPW], float (&u)[RPW]) {
@@ -222,20 +222,16 @@ __device__ __forceinline__ void gate_up_token(const uint8_t *xr, int n_chunks, i
                     g[i] = dot_f32_f32(wg[i][n], xv, g[i]);
                     u[i] = dot_f32_f32(wu[i][n], xv, u[i]);
                 }
-            } else {  // W_Q4: one 32-element block per chunk
-                uint32_t xw[16], xp[16];
+            } else {  // W_Q4: one 32-element block per chunk; the stage holds the token in
+                      // the pair order of the weight decode and each block's bias 136 * sum x,
+                      // so sum_e (128 + u_e) x_e - bias = sum_e q_e x_e
+                uint32_t xp[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint4 v = *reinterpret_cast<const uint4 *>(xr + 64 * c + 16 * q);
-                    xw[4 * q + 0] = v.x; xw[4 * q + 1] = v.y;
-                    xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
+                    xp[4 * q + 0] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
                 }
-                float xsum = 0.f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) xsum += bf16_lo(xw[q]) + bf16_hi(xw[q]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) bf16x8_to_q4_order(xw + 4 * q, xp + 4 * q);
-                const float bias = 136.0f * xsum;  // (128 + 8) * sum x
+                const float bias = xbr[c];
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
                     g[i] = fmaf(sg[i][n], dot_q4_bf16(wg[i][n], xp) - bias, g[i]);
@@ -244,6 +240,14 @@ __device__ __forceinline__ void gate_up_token(const uint8_t *xr, int n_chunks, i
             }
         }
     }
+}
+
+// Bytes of the token stage: the tokens, and for 4-bit rows each block's bias after them.
+__host__ __device__ inline size_t stage_x_bytes(int toks, int H, int xbytes) {
+    return ((size_t)toks * H * xbytes + 15) & ~(size_t)15;
+}
+__host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int sums) {
+    return stage_x_bytes(toks, H, xbytes) + (sums ? (((size_t)toks * (H / 32) * 4 + 15) & ~(size_t)15) : 0);
 }
 
 template <int WK, int LPR, int NC>
@@ -259,6 +263,29 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     const int n_chunks = (int)(row_bytes<WK>(H) / 16);
     const int npairs = T * k;
     const size_t xrow = (size_t)H * XB;
+    // 4-bit rows: each block's activation bias, after the staged tokens
+    float *xbias = reinterpret_cast<float *>(lds + stage_x_bytes(p.x_resident ? T : p.tok_per_pass, H, XB));
+    const int nblk = H / 32;
+    // chunk i of the stage (16 bytes of one token's row; a block is 4 chunks held by 4
+    // neighbouring lanes, which execute together): 4-bit rows keep the chunk in the
+    // pair order of the weight decode, and the block's first lane writes its bias
+    auto stage_store = [&](int i, uint4 v, bool ok) {
+        if constexpr (WK == W_Q4) {
+            const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
+            uint32_t xp[4];
+            bf16x8_to_q4_order(xw, xp);
+            float sx = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                       ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+            sx = sx + dpp_f<kDppXor1>(sx);
+            sx = sx + dpp_f<kDppXor2>(sx);
+            if (ok) {
+                reinterpret_cast<uint4 *>(lds)[i] = make_uint4(xp[0], xp[1], xp[2], xp[3]);
+                if ((i & 3) == 0) xbias[i >> 2] = 136.0f * sx;  // (128 + 8) * sum x
+            }
+        } else {
+            if (ok) reinterpret_cast<uint4 *>(lds)[i] = v;
+        }
+    };
     // routing tables: global (routed by the router launch) or this workgroup's LDS
     const int *recs = p.records, *prs = p.pairs;
     int nu = 0;
@@ -288,6 +315,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     const int n16 = p.x_resident ? (int)(T * xrow / 16) : 0;
     const bool x_early = route_here && n16 <= kXPre * 256;
     uint4 xpre[kXPre];
+#pragma unroll
+    for (int q = 0; q < kXPre; ++q) xpre[q] = make_uint4(0, 0, 0, 0);
     if (x_early) {
 #pragma unroll
         for (int q = 0; q < kXPre; ++q) {
@@ -321,12 +350,17 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
 #pragma unroll
         for (int q = 0; q < kXPre; ++q) {
             const int i = tid + 256 * q;
-            if (i < n16) reinterpret_cast<uint4 *>(lds)[i] = xpre[q];
+            stage_store(i, xpre[q], i < n16);
         }
         __syncthreads();
     } else if (p.x_resident) {
-        for (int i = tid; i < n16; i += 256)
-            reinterpret_cast<uint4 *>(lds)[i] = ld16((const uint8_t *)p.x + 16 * (size_t)i);
+        // rounds of 4 chunks per thread (all loads of a round in flight together)
+        for (int b = 0; b < n16; b += 1024) {
+            uint4 xv[4];
+            load_chunks<4>(xv, n16 - b, tid, [&](int i) { return (const uint8_t *)p.x + 16 * (size_t)(b + i); });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) stage_store(b + tid + 256 * q, xv[q], b + tid + 256 * q < n16);
+        }
         __syncthreads();
     }
 
@@ -340,16 +374,22 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
             const int nt = min(tpp, job.ntok - t0);
             if (!p.x_resident) {
                 __syncthreads();
-                const int xr16 = (int)(xrow / 16);
-                for (int i = tid; i < nt * xr16; i += 256) {
+                // rounds of 4 chunks per thread (all loads of a round in flight together)
+                const int xr16 = (int)(xrow / 16), n16p = nt * xr16;
+                for (int b = 0; b < n16p; b += 1024) {
+                uint4 xv[4];
+                load_chunks<4>(xv, n16p - b, tid, [&](int ii) {
+                    const int i = b + ii;
                     const int a = i / xr16, c = i - a * xr16;
                     int tok = t0 + a;
                     if (job.routed) {
                         const int pr = job_pair(job.rec, prs, t0 + a);
                         tok = (pr >= 0 && pr < npairs) ? pr / k : 0;
                     }
-                    reinterpret_cast<uint4 *>(lds)[i] =
-                        ld16((const uint8_t *)p.x + (size_t)tok * xrow + 16 * (size_t)c);
+                    return (const uint8_t *)p.x + (size_t)tok * xrow + 16 * (size_t)c;
+                });
+#pragma unroll
+                for (int q = 0; q < 4; ++q) stage_store(b + tid + 256 * q, xv[q], b + tid + 256 * q < n16p);
                 }
                 __syncthreads();
             }
@@ -360,9 +400,10 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                     tok = orow / k;
                 }
                 const bool ook = orow >= 0 && orow < (job.routed ? npairs : T);
-                const uint8_t *xr = lds + (p.x_resident ? (size_t)(ook ? tok : 0) : (size_t)a) * xrow;
+                const size_t srow = p.x_resident ? (size_t)(ook ? tok : 0) : (size_t)a;
+                const uint8_t *xr = lds + srow * xrow;
                 float g[RPW], u[RPW];
-                gate_up_token<WK, LPR, NC, RPW>(xr, n_chunks, sl, wg, wu, sg, su, g, u);
+                gate_up_token<WK, LPR, NC, RPW>(xr, xbias + srow * nblk, n_chunks, sl, wg, wu, sg, su, g, u);
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
                     const int r = job.tile * RPWG + (wave * RPW + i) * RPI + seg;
@@ -676,13 +717,13 @@ __global__ __launch_bounds__(256) void k_join(JoinParams p) {
 
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes) {
     const int toks = p.x_resident ? p.T : p.tok_per_pass;
-    const size_t stage = ((size_t)toks * p.H * xbytes + 15) & ~(size_t)15;
+    const size_t stage = stage_bytes(toks, p.H, xbytes, p.x_sums);
     return stage + (p.routed && p.route_here ? route_lds_layout(p.T, p.k, p.E, true).bytes : 0);
 }
 
 int gate_up_route_lds_off(const GateUpParams &p, int xbytes) {
     const int toks = p.x_resident ? p.T : p.tok_per_pass;
-    return (int)(((size_t)toks * p.H * xbytes + 15) & ~(size_t)15);
+    return (int)stage_bytes(toks, p.H, xbytes, p.x_sums);
 }
 
 hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int grid, hipStream_t s) {

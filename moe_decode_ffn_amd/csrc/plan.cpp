@@ -133,7 +133,6 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
 
     const int H = d.hidden, E = d.n_experts, k = d.top_k, I = d.inter, Is = d.shared_inter;
     const size_t T = (size_t)d.max_tokens, P_ = T * k;
-    P->map_router = make_row_map(row_bytes_of(W_F32, H));
     P->map_gu = make_row_map(row_bytes_of(P->wkind, H));
     P->map_down = make_row_map(row_bytes_of(P->wkind, std::max(I, Is)));
 
@@ -142,7 +141,7 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     RouterParams rq{};
     rq.H = H; rq.x_bf16 = xbytes == 2;
     rq.tok_tile = std::max(1, std::min(8, (int)(kStageBytes / ((size_t)H * xbytes))));
-    const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && P->map_router.nc <= 32;
+    const bool maps_ok = P->map_gu.nc <= 16 && P->map_down.nc <= 16 && router_chunks_per_lane(H) <= 8;
     if (!maps_ok || router_lds_bytes(rq) > kLdsLimit) {
         delete P;
         return set_error(MOE_FFN_ERR_UNSUPPORTED, "shapes exceed the per-workgroup LDS budget");
@@ -164,7 +163,7 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
     L.n_unique = c;   c += align_up(16);
     L.pairs = c;      c += align_up(P_ * 4);
     L.pos_expert = c; c += align_up(P_ * 4);
-    L.logits = c;     c += align_up(T * (E + 1) * 4);
+    L.logits = c;     c += align_up(T * logit_stride(E) * 4);
     // normalised input of both branches (x_dtype), router -> experts
     L.xn = c;         c += (d.flags & MOE_FFN_INPUT_NORM) ? align_up(T * H * xbytes) : 0;
     // batch routing's counts, prefixes and ranks (batches above kRouteKernelMax)

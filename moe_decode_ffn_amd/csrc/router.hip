@@ -46,26 +46,28 @@ __device__ __forceinline__ float seg_sum8(const float (&a)[8], int sl, int &tok)
     return v;
 }
 
-int router_rows_per_wg(const RowMap &m) { return kRouterWaves * (64 / m.lpr); }
-
-template <int LPR, int NC, bool XBF>
+// One workgroup per row (E router rows, then the gate vector as row E) and token
+// tile: the four waves split the row into quarters, so the E+1 rows spread over
+// every CU and each lane issues only its few 16-byte loads.  Lane l of wave w holds
+// chunks w*CPW + l + 64n (n < NC) of the fp32 row.
+template <int NC, bool XBF>
 __global__ __launch_bounds__(256) void k_router(RouterParams p) {
-    constexpr int RPI = 64 / LPR;
     extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ float s_part[kRouterWaves][2][kRouterTile];  // per wave: dot products, squares
+    __shared__ float s_rho[kRouterTile];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int seg = lane / LPR, sl = lane % LPR;
     const int H = p.H, E = p.E;
-    const int n_chunks = H / 4;  // fp32 rows, 4 elements per 16-byte chunk
-    const int row = (blockIdx.x * kRouterWaves + wave) * RPI + seg;
-    const bool valid = row <= E;
+    const int n_chunks = H / 4;            // fp32 rows, 4 elements per 16-byte chunk
+    const int cpw = n_chunks / kRouterWaves;  // chunks per wave (H is a multiple of 32)
+    const int row = blockIdx.x;
     const float *W = row < E ? p.router + (size_t)row * H : p.gate_vec;
 
     float4 w[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const int c = sl + LPR * n;
-        w[n] = (valid && c < n_chunks) ? *reinterpret_cast<const float4 *>(W + 4 * c)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int q = lane + 64 * n;
+        w[n] = q < cpw ? *reinterpret_cast<const float4 *>(W + 4 * (wave * cpw + q))
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
     // input RMSNorm folded into the dot products: logit = rho * sum_h (W[h] * g[h]) * x[h],
@@ -77,24 +79,31 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
     float4 gn[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const int c = sl + LPR * n;
-        gn[n] = (norm && c < n_chunks) ? *reinterpret_cast<const float4 *>(p.norm_w + 4 * c)
-                                       : make_float4(1.f, 1.f, 1.f, 1.f);
+        const int q = lane + 64 * n;
+        gn[n] = (norm && q < cpw) ? *reinterpret_cast<const float4 *>(p.norm_w + 4 * (wave * cpw + q))
+                                  : make_float4(1.f, 1.f, 1.f, 1.f);
     }
 
     const int t0 = blockIdx.y * p.tok_tile;
     const int nt = min(p.tok_tile, p.T - t0);
-    // the normalised tokens of the tile are written by the column's workgroups in
-    // order, one 4-element chunk per thread and pass; the first chunk's norm weights
-    // are fetched now as well
+    // the normalised tokens of the tile are written by the column's first workgroups,
+    // one 4-element chunk per thread and pass; the first chunk's norm weights are
+    // fetched now as well
     const int xn_units = norm ? nt * n_chunks : 0;
     const int xn_u0 = blockIdx.x * 256 + tid;
     float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (xn_u0 < xn_units) g0 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * (xn_u0 % n_chunks));
     const int xrow = H * (XBF ? 2 : 4);
     const uint8_t *xs = (const uint8_t *)p.x + (size_t)t0 * xrow;
-    for (int i = tid; i < nt * xrow / 16; i += 256)
-        reinterpret_cast<uint4 *>(lds)[i] = ld16(xs + 16 * (size_t)i);
+    {
+        // the tile is at most kStageBytes: 8 chunks per thread
+        const int n16 = nt * xrow / 16;
+        uint4 xv[8];
+        load_chunks<8>(xv, n16, tid, [&](int i) { return xs + 16 * (size_t)i; });
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (tid + 256 * q < n16) reinterpret_cast<uint4 *>(lds)[tid + 256 * q] = xv[q];
+    }
     __syncthreads();
     if (norm) {
 #pragma unroll
@@ -111,14 +120,16 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         }
     };
 
-    // partial dot products of up to 8 tokens, then one transposed reduction for all
+    // partial dot products of up to 8 tokens, one transposed reduction per wave for all,
+    // then the four quarters summed in wave order
     float acc[kRouterTile], ss[kRouterTile];
 #pragma unroll
     for (int i = 0; i < kRouterTile; ++i) acc[i] = ss[i] = 0.f;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const int c = sl + LPR * n;
-        if (c < n_chunks) {
+        const int q = lane + 64 * n;
+        if (q < cpw) {
+            const int c = wave * cpw + q;
 #pragma unroll
             for (int i = 0; i < kRouterTile; ++i) {
                 if (i < nt) {
@@ -138,40 +149,45 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         }
     }
     int tok = 0;
-    float sum = seg_sum8<LPR>(acc, sl, tok);
-    const bool writer = (sl & (LPR / 8 - 1)) == 0 && tok < nt;
-    float rho = 1.f;
-    if (norm) {
-        const float sq = seg_sum8<LPR>(ss, sl, tok);
-        rho = 1.0f / sqrtf(sq / (float)H + p.norm_eps);
-        sum *= rho;
+    const float sum = seg_sum8<64>(acc, lane, tok);
+    const float sq = norm ? seg_sum8<64>(ss, lane, tok) : 0.f;
+    if ((lane & 7) == 0) {
+        s_part[wave][0][tok] = sum;
+        s_part[wave][1][tok] = sq;
     }
-    if (valid && writer) p.logits[(size_t)(t0 + tok) * (E + 1) + row] = sum;
-    if (norm) {
+    __syncthreads();
+    if (tid < nt) {
+        float v = ((s_part[0][0][tid] + s_part[1][0][tid]) + s_part[2][0][tid]) + s_part[3][0][tid];
+        float rho = 1.f;
+        if (norm) {
+            const float q = ((s_part[0][1][tid] + s_part[1][1][tid]) + s_part[2][1][tid]) + s_part[3][1][tid];
+            rho = 1.0f / sqrtf(q / (float)H + p.norm_eps);
+            v *= rho;
+            s_rho[tid] = rho;
+        }
+        p.logits[(size_t)(t0 + tid) * logit_stride(E) + row] = v;
+    }
+    if (norm && blockIdx.x * 256 < xn_units) {
         // the normalised tokens, (x * rho) * g, that feed both expert branches, rounded
         // to the activation storage
-        if (blockIdx.x * 256 < xn_units) {
-            __shared__ float s_rho[kRouterTile];
-            if (wave == 0 && seg == 0 && writer) s_rho[tok] = rho;
-            __syncthreads();
-            for (int q = xn_u0; q < xn_units; q += 256 * gridDim.x) {
-                const int i = q / n_chunks, c = q - i * n_chunks;
-                const float r = s_rho[i];
-                const float4 xv = x_chunk(i, c);
-                const float4 g = q == xn_u0 ? g0 : *reinterpret_cast<const float4 *>(p.norm_w + 4 * c);
-                const float v0 = __fmul_rn(__fmul_rn(xv.x, r), g.x), v1 = __fmul_rn(__fmul_rn(xv.y, r), g.y);
-                const float v2 = __fmul_rn(__fmul_rn(xv.z, r), g.z), v3 = __fmul_rn(__fmul_rn(xv.w, r), g.w);
-                const size_t o = (size_t)(t0 + i) * H + 4 * c;
-                if constexpr (XBF) {
-                    uint2 b;
-                    b.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
-                    b.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.xn) + o) = b;
-                } else {
-                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.xn) + o) = make_float4(v0, v1, v2, v3);
-                }
+        __syncthreads();
+        for (int q = xn_u0; q < xn_units; q += 256 * gridDim.x) {
+            const int i = q / n_chunks, c = q - i * n_chunks;
+            const float r = s_rho[i];
+            const float4 xv = x_chunk(i, c);
+            const float4 g = q == xn_u0 ? g0 : *reinterpret_cast<const float4 *>(p.norm_w + 4 * c);
+            const float v0 = __fmul_rn(__fmul_rn(xv.x, r), g.x), v1 = __fmul_rn(__fmul_rn(xv.y, r), g.y);
+            const float v2 = __fmul_rn(__fmul_rn(xv.z, r), g.z), v3 = __fmul_rn(__fmul_rn(xv.w, r), g.w);
+            const size_t o = (size_t)(t0 + i) * H + 4 * c;
+            if constexpr (XBF) {
+                uint2 b;
+                b.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
+                b.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.xn) + o) = b;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.xn) + o) = make_float4(v0, v1, v2, v3);
             }
         }
     }
@@ -309,7 +325,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
         for (int v = 0; v < 4; ++v) {
             const int e = blockIdx.x * 16 + 4 * g + v;
             const float sum = ((acc[n][v] + s_part[0][n][v][lane]) + s_part[1][n][v][lane]) + s_part[2][n][v][lane];
-            if (e <= E) p.logits[(size_t)t * (E + 1) + e] = sum;
+            if (e <= E) p.logits[(size_t)t * logit_stride(E) + e] = sum;
         }
     }
 }
@@ -363,7 +379,7 @@ __global__ __launch_bounds__(256) void k_rank_batch(RouterParams p) {
         RouteOut o{p.ids + (size_t)t * k, p.wts + (size_t)t * k, p.gate_s + t,
                    p.dbg_ids ? p.dbg_ids + (size_t)t * k : nullptr, p.dbg_w ? p.dbg_w + (size_t)t * k : nullptr,
                    p.dbg_gate ? p.dbg_gate + t : nullptr, p.dbg_logits ? p.dbg_logits + (size_t)t * E : nullptr};
-        route_token_any(p.logits + (size_t)t * (E + 1), E, k, lane, o);
+        route_token_any(p.logits + (size_t)t * logit_stride(E), E, k, lane, o);
         if (lane < k) s_ids[lt * k + lane] = o.ids[lane];  // this lane's own store
     }
     __syncthreads();
@@ -505,31 +521,31 @@ size_t router_lds_bytes(const RouterParams &p) {
     return (size_t)p.tok_tile * p.H * (p.x_bf16 ? 2 : 4);
 }
 
-template <int LPR, int NC>
-static hipError_t launch_router_t(const RouterParams &p, int grid_rows, int grid_tiles,
-                                  hipStream_t s) {
+template <int NC>
+static hipError_t launch_router_t(const RouterParams &p, int grid_tiles, hipStream_t s) {
     const size_t lds = router_lds_bytes(p);
-    const dim3 grid(grid_rows, grid_tiles);
+    const dim3 grid(p.E + 1, grid_tiles);
     if (p.x_bf16)
-        launch_kernel(k_router<LPR, NC, true>, grid, dim3(256), lds, s, p);
+        launch_kernel(k_router<NC, true>, grid, dim3(256), lds, s, p);
     else
-        launch_kernel(k_router<LPR, NC, false>, grid, dim3(256), lds, s, p);
+        launch_kernel(k_router<NC, false>, grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_router(const RouterParams &p, const RowMap &m, int grid_rows, int grid_tiles,
-                         hipStream_t s) {
-    if (router_lds_bytes(p) > kLdsLimit) return hipErrorInvalidValue;
-    switch (m.lpr * 100 + m.nc) {
-    case 801: return launch_router_t<8, 1>(p, grid_rows, grid_tiles, s);
-    case 1601: return launch_router_t<16, 1>(p, grid_rows, grid_tiles, s);
-    case 3201: return launch_router_t<32, 1>(p, grid_rows, grid_tiles, s);
-    case 6401: return launch_router_t<64, 1>(p, grid_rows, grid_tiles, s);
-    case 6402: return launch_router_t<64, 2>(p, grid_rows, grid_tiles, s);
-    case 6404: return launch_router_t<64, 4>(p, grid_rows, grid_tiles, s);
-    case 6408: return launch_router_t<64, 8>(p, grid_rows, grid_tiles, s);
-    case 6416: return launch_router_t<64, 16>(p, grid_rows, grid_tiles, s);
-    case 6432: return launch_router_t<64, 32>(p, grid_rows, grid_tiles, s);
+int router_chunks_per_lane(int H) {
+    const int per_wave = H / 4 / kRouterWaves;
+    int nc = 1;
+    while (64 * nc < per_wave) nc <<= 1;
+    return nc;
+}
+
+hipError_t launch_router(const RouterParams &p, int grid_tiles, hipStream_t s) {
+    if (router_lds_bytes(p) > kStageBytes || p.tok_tile > kRouterTile || p.H % 32 != 0) return hipErrorInvalidValue;
+    switch (router_chunks_per_lane(p.H)) {
+    case 1: return launch_router_t<1>(p, grid_tiles, s);
+    case 2: return launch_router_t<2>(p, grid_tiles, s);
+    case 4: return launch_router_t<4>(p, grid_tiles, s);
+    case 8: return launch_router_t<8>(p, grid_tiles, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -28,31 +28,21 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Largest / smallest value over the wave, in every lane, in vector registers only
-// (no round trip through scalar registers): a butterfly inside each row of 16 lanes
-// (DPP), then the rows combined by swapping the two halves of the wave and then
-// neighbouring rows (gfx950 permlane swaps), taking the max (min) of each lane's
-// value and the swapped one.
+// Largest value over the wave, in every lane, in vector registers only (no round
+// trip through scalar registers): a butterfly inside each row of 16 lanes (DPP),
+// then the rows combined by swapping the two halves of the wave and then
+// neighbouring rows (gfx950 permlane swaps), taking the max of each lane's value
+// and the swapped one.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xf, 0xf, false));
+    // update_dpp with bound_ctrl lets the compiler fold each move into the max (v_max_u32_dpp)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xf, 0xf, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xf, 0xf, true));
     const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     v = max((uint32_t)a[0], (uint32_t)a[1]);
     const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return max((uint32_t)b[0], (uint32_t)b[1]);
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xf, 0xf, false));
-    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    v = min((uint32_t)a[0], (uint32_t)a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return min((uint32_t)b[0], (uint32_t)b[1]);
 }
 
 // The logit of a key (the inverse of logit_key; a -0 logit comes back as +0, which
@@ -61,44 +51,66 @@ __device__ __forceinline__ float key_logit(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// One wave ranks one token.  lg: E+1 logits (column E = shared-gate logit).
-// Expert e = lane * EPL + i sits in register slot i of its lane.  The k picks
-// are taken one per round in rank order: the largest remaining key over the
-// wave, and among equal keys the lowest expert index (the smallest index of a
-// slot holding that key, over the wave); the pick's slot is cleared and lane r
-// keeps pick r.  Keys of real logits are at least 1 (0 marks a taken or
-// padding slot), so the picks are k distinct experts whatever the logits hold.
-// A round is a chain of dependent vector instructions (its cost is their issue
-// latency, ~7 cycles each for one wave).
+// Orders two (key, index) slots of a lane: larger key first, and among equal keys
+// the lower expert index first.
+__device__ __forceinline__ void slot_order(uint32_t &ka, uint32_t &ia, uint32_t &kb, uint32_t &ib) {
+    const bool swap = kb > ka || (kb == ka && ib < ia);
+    const uint32_t k0 = swap ? kb : ka, k1 = swap ? ka : kb;
+    const uint32_t i0 = swap ? ib : ia, i1 = swap ? ia : ib;
+    ka = k0; kb = k1; ia = i0; ib = i1;
+}
+
+// One wave ranks one token.  lg: the token's logits row (16-byte aligned, E router
+// logits, the shared-gate logit at column E).  Expert e = lane * EPL + i starts in
+// register slot i of its lane; each lane first sorts its EPL slots (key descending,
+// index ascending), so its head is its best remaining expert.  The k picks are then
+// taken one per round in rank order: the largest head over the wave, and among equal
+// heads the lowest lane (lanes hold ascending index ranges, so that is the lowest
+// expert index); the winning lane pops its head and lane r keeps pick r.  Keys of
+// real logits are at least 1 (0 marks an empty slot), so the picks are k distinct
+// experts whatever the logits hold.
 // Weights: p_e = exp(l_e - max l) / sum_all exp(.) renormalised over the picks
 // is w_j = exp(l_j - m) / sum_picks exp(l_i - m) for any m (the full sum
 // cancels); m = the first pick, the largest logit.
 template <int EPL>
 __device__ void route_token(const float *lg, int E, int k, int lane, const RouteOut &o) {
-    uint32_t key[EPL];
+    uint32_t key[EPL], idx[EPL];
+    if constexpr (EPL % 4 == 0) {
+        // whole 16-byte groups: a group that starts below E lies inside the padded row
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        key[i] = e < E ? max(logit_key(lg[e]), 1u) : 0u;
+        for (int v = 0; v < EPL / 4; ++v) {
+            const int e0 = lane * EPL + 4 * v;
+            const float4 f = e0 < E ? *reinterpret_cast<const float4 *>(lg + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) key[4 * v + q] = e0 + q < E ? max(logit_key(fv[q]), 1u) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            key[i] = e < E ? max(logit_key(lg[e]), 1u) : 0u;
+        }
     }
     const float glog = lg[E];
-    uint32_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) best = max(best, key[i]);
+    for (int i = 0; i < EPL; ++i) idx[i] = (uint32_t)(lane * EPL + i);
+    // in-lane sort: odd-even transposition, EPL rounds
+#pragma unroll
+    for (int r = 0; r < EPL; ++r)
+#pragma unroll
+        for (int i = r & 1; i + 1 < EPL; i += 2) slot_order(key[i], idx[i], key[i + 1], idx[i + 1]);
 
     uint32_t my_id = 0, my_key = 0;
     for (int r = 0; r < k; ++r) {
-        const uint32_t M = wave_max_u32(best);
-        uint32_t cand = 0xffffffffu;
+        const uint32_t M = wave_max_u32(key[0]);
+        const unsigned long long hit = __ballot(key[0] == M);
+        const int wl = (int)__builtin_ctzll(hit);
+        const uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], wl);
+        if (lane == wl) {
 #pragma unroll
-        for (int i = EPL - 1; i >= 0; --i)
-            if (key[i] == M) cand = (uint32_t)(lane * EPL + i);
-        const uint32_t win = wave_min_u32(cand);
-        best = 0u;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            if ((uint32_t)(lane * EPL + i) == win) key[i] = 0u;
-            best = max(best, key[i]);
+            for (int i = 0; i + 1 < EPL; ++i) { key[i] = key[i + 1]; idx[i] = idx[i + 1]; }
+            key[EPL - 1] = 0u;
         }
         if (lane == r) { my_id = win; my_key = M; }
     }
@@ -135,50 +147,87 @@ __host__ __device__ inline int bucket_scratch_ints(int E, int T) {
     return E * ((T + 31) / 32) + 2 * E + 2 * 16 + 16;
 }
 
-// Bucketing of up to 64 pairs by one wave (same results as bucket_pairs):
-// lane q holds pair q; its position is the number of pairs with a smaller
-// expert plus the pairs of the same expert with a smaller pair id.
+// The value of lane (lane ^ J) for J a power of two below 64, in vector registers
+// only: DPP within rows of 16 lanes (xor 4 = half mirror then reversed quads, xor 8 =
+// mirror then half mirror), the gfx950 permlane swaps across rows.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xf, 0xf, true);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xf, 0xf, true);
+    } else if constexpr (J == 4) {
+        const int m = __builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, m, kDppRevQuad, 0xf, 0xf, true);
+    } else if constexpr (J == 8) {
+        const int m = __builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, m, kDppHalfMirror, 0xf, 0xf, true);
+    } else if constexpr (J == 16) {
+        const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? (uint32_t)a[0] : (uint32_t)a[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? (uint32_t)a[0] : (uint32_t)a[1];
+    }
+}
+
+// One stage of a bitonic sort over the wave (ascending over lanes): blocks of KK lanes
+// alternate direction, partners at distance J keep the smaller / larger key.
+template <int KK, int J>
+__device__ __forceinline__ uint32_t bitonic_stage(uint32_t key, int lane) {
+    const uint32_t other = lane_xor<J>(key, lane);
+    const bool up = (lane & KK) == 0, lower = (lane & J) == 0;
+    return (lower == up) ? min(key, other) : max(key, other);
+}
+
+// Bucketing of up to 64 pairs by one wave (the same tables as bucket_pairs): lane q
+// holds pair q as the key expert * 64 + q; a bitonic sort over the wave puts the keys
+// in (expert, pair) order, so lane q then holds bucket position q; a bucket starts
+// where the expert changes from the lane below, and its slot is the number of bucket
+// starts below it.  All 64 lanes of the wave must be active.
 __device__ inline void bucket_pairs_wave(const int *ids, int NP, int E, int4 *slots, int *pairs,
                                          int *pos_expert, int *n_unique) {
     const int lane = threadIdx.x & 63;
-    const int e = lane < NP ? ids[lane] : 0x7fffffff;
-    const bool ok = lane < NP && e >= 0 && e < E;
-    // ids is 16-byte aligned and the LDS behind it is readable, so it is read
-    // four entries at a time; entries at or past NP are masked out
-    const int4 *ids4 = reinterpret_cast<const int4 *>(ids);
-    int smaller = 0, same_before = 0, same = 0;
-#pragma unroll 4
-    for (int j0 = 0; j0 < NP; j0 += 4) {
-        const int4 q = ids4[j0 >> 2];
-        const int qa[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r, ej = qa[r];
-            const bool vj = j < NP && ej >= 0 && ej < E;  // an out-of-range id takes no position
-            smaller += (vj && ej < e) ? 1 : 0;
-            same += (vj && ej == e) ? 1 : 0;
-            same_before += (vj && ej == e && j < lane) ? 1 : 0;
-        }
-    }
-    const bool first = ok && same_before == 0;
+    const int e0 = lane < NP ? ids[lane] : -1;
+    uint32_t key = (e0 >= 0 && e0 < E) ? ((uint32_t)e0 << 6) | (uint32_t)lane : 0xffffffffu;
+    key = bitonic_stage<2, 1>(key, lane);
+    key = bitonic_stage<4, 2>(key, lane);
+    key = bitonic_stage<4, 1>(key, lane);
+    key = bitonic_stage<8, 4>(key, lane);
+    key = bitonic_stage<8, 2>(key, lane);
+    key = bitonic_stage<8, 1>(key, lane);
+    key = bitonic_stage<16, 8>(key, lane);
+    key = bitonic_stage<16, 4>(key, lane);
+    key = bitonic_stage<16, 2>(key, lane);
+    key = bitonic_stage<16, 1>(key, lane);
+    key = bitonic_stage<32, 16>(key, lane);
+    key = bitonic_stage<32, 8>(key, lane);
+    key = bitonic_stage<32, 4>(key, lane);
+    key = bitonic_stage<32, 2>(key, lane);
+    key = bitonic_stage<32, 1>(key, lane);
+    key = bitonic_stage<64, 32>(key, lane);
+    key = bitonic_stage<64, 16>(key, lane);
+    key = bitonic_stage<64, 8>(key, lane);
+    key = bitonic_stage<64, 4>(key, lane);
+    key = bitonic_stage<64, 2>(key, lane);
+    key = bitonic_stage<64, 1>(key, lane);
+    const bool ok = key != 0xffffffffu;
+    const int e = (int)(key >> 6);
+    const int below = __shfl_up(e, 1);
+    const bool first = ok && (lane == 0 || below != e);
     const unsigned long long fm = __ballot(first);
-    // slot of this lane's expert: first lanes of smaller experts
-    int u = 0;
-#pragma unroll 4
-    for (int j0 = 0; j0 < NP; j0 += 4) {
-        const int4 q = ids4[j0 >> 2];
-        const int qa[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            u += (j < NP && ((fm >> j) & 1ull) && qa[r] < e) ? 1 : 0;
-        }
-    }
+    const int nvalid = __popcll(__ballot(ok));  // valid pairs: the last bucket ends there
     if (ok) {
-        pairs[smaller + same_before] = lane;
-        pos_expert[smaller + same_before] = e;
+        pairs[lane] = (int)(key & 63u);
+        pos_expert[lane] = e;
     }
-    if (first) slots[u] = make_int4(e, smaller, same, 0);
+    if (first) {
+        const int u = __popcll(fm & ((1ull << lane) - 1ull));
+        const unsigned long long after = lane == 63 ? 0ull : fm & ~((2ull << lane) - 1ull);
+        const int end = after ? (int)__builtin_ctzll(after) : nvalid;
+        slots[u] = make_int4(e, lane, end - lane, 0);
+    }
     if (lane == 0) *n_unique = __popcll(fm);
 }
 
@@ -314,7 +363,7 @@ __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int 
                    g.dbg_ids ? g.dbg_ids + t * k : nullptr, g.dbg_w ? g.dbg_w + t * k : nullptr,
                    g.dbg_gate ? g.dbg_gate + t : nullptr,
                    g.dbg_logits ? g.dbg_logits + (size_t)t * E : nullptr};
-        route_token_any(logits + (size_t)t * (E + 1), E, k, lane, o);
+        route_token_any(logits + (size_t)t * logit_stride(E), E, k, lane, o);
     }
 }
 
@@ -343,7 +392,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
             }
             if (j == 0) *nup = k;
         }
-    } else if (NP <= 16) {  // measured: one wave wins up to 16 pairs, the whole workgroup above
+    } else if (NP <= 64) {  // one wave sorts the pairs (no barrier inside)
         if (threadIdx.x < 64) bucket_pairs_wave(ids, NP, E, slots, pairs, pose, nup);
     } else {
         bucket_pairs(ids, T, k, E, reinterpret_cast<uint32_t *>(area + L.scratch), slots, pairs, pose, nup);

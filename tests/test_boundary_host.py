@@ -115,6 +115,10 @@ def test_plan_null_arguments(lib):
     lib.moe_ffn_destroy(None)  # no-op
 
 
+def _logit_stride(E):
+    return (E + 1 + 3) // 4 * 4
+
+
 def _align(v):
     return (v + 255) // 256 * 256
 
@@ -138,9 +142,10 @@ def test_workspace_is_shared_plus_routing_plus_max_of_phases(lib, T):
     ffn.moe_ffn_destroy(plan)
     shared = _align(T * Is * 4) + _align(T * H * 4)
     # routing region: gate, ids, weights, one 64-byte job record per expert, used-expert
-    # count, bucketed pairs and their experts, logits [T][E+1], batch routing's ints
+    # count, bucketed pairs and their experts, logits [T][E+1 padded to a multiple of 4],
+    # batch routing's ints
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4))
+               + 2 * _align(T * k * 4) + _align(T * _logit_stride(E) * 4))
     routing += _align(_batch_routing_ints(T, k, E) * 4) if T > 16 else 0
     h, y = _align(T * k * I * 4), _align(T * k * H * 4)
     phases = {"gate/up": h, "down": h + y, "join": y}  # live scratch of each sequential step
@@ -188,7 +193,7 @@ def test_workspace_with_batch_routing(lib, T):
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
+               + 2 * _align(T * k * 4) + _align(T * _logit_stride(E) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
     assert info.routing_region_bytes == routing
     assert ws == info.workspace_bytes == (_align(T * Is * 4) + _align(T * H * 4) + routing
                                           + _align(T * k * I * 4) + _align(T * k * H * 4))
@@ -202,7 +207,7 @@ def test_plan_with_the_largest_expert_count_and_top_k(lib):
     info = ffn.moe_ffn_plan_get_info(plan)
     ffn.moe_ffn_destroy(plan)
     routing = (_align(T * 4) + 2 * _align(T * k * 4) + _align(E * 64) + _align(16)
-               + 2 * _align(T * k * 4) + _align(T * (E + 1) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
+               + 2 * _align(T * k * 4) + _align(T * _logit_stride(E) * 4) + _align(_batch_routing_ints(T, k, E) * 4))
     assert info.routing_region_bytes == routing
 
 
