@@ -82,13 +82,19 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
 // Chunk loads of a 256-thread staging pass: thread tid takes chunks tid + 256q
 // (q < MAXC, below n), every load issued before any is used, so a pass costs one
 // memory round trip, not one per chunk (a plain loop waits for each load before
-// the next).  src(i) gives chunk i's address; a chunk at or past n reads as zero.
+// the next).  src(i) gives chunk i's address; src(0) must be readable even when n is
+// 0.  Every thread issues all MAXC loads (a chunk at or past n re-reads the address
+// of chunk n - 1, or of chunk 0, and is to be ignored): with a fixed number of loads in
+// flight the compiler waits for exactly the ones a later use needs, not for all
+// (memory returns loads in issue order; a conditional load would make it wait for
+// every load issued before the use).
 template <int MAXC, typename Src>
 __device__ __forceinline__ void load_chunks(uint4 (&v)[MAXC], int n, int tid, Src src) {
+    const int last = n > 0 ? n - 1 : 0;
 #pragma unroll
     for (int q = 0; q < MAXC; ++q) {
         const int i = tid + 256 * q;
-        v[q] = i < n ? ld16(src(i)) : make_uint4(0, 0, 0, 0);
+        v[q] = ld16(src(i < n ? i : last));
     }
 }
 

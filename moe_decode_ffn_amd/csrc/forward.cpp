@@ -257,7 +257,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
         GateUpParams q = gp;
         q.routed = 1;
         q.route_here = 1;
-        gp.route_here = !gemm && Ti <= kRouteInGateUpMax &&
+        // (the prologue holds the batch's logits rows in at most 5 chunks per thread)
+        gp.route_here = !gemm && Ti <= kRouteInGateUpMax && (size_t)Ti * logit_stride((int)E) / 4 <= 5 * 256 &&
                         gate_up_lds_bytes(q, (int)xb) <= kLdsLimit ? 1 : 0;
         gp.route_lds_off = gate_up_route_lds_off(q, (int)xb);
     }

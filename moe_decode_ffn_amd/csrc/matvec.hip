@@ -20,6 +20,7 @@
 // Storage: fp32, bf16, or 4-bit blocks (32 elements + one fp16 scale per block,
 // dequantised in registers).
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -170,10 +171,16 @@ __device__ __forceinline__ Job decode_job(int j, int tiles_shared, int tiles_rou
 }
 
 // Loads this lane's chunks of the job's rows (RPW rows per wave, NC chunks each).
+// Every load is issued, whether or not the row or chunk exists: one that does not
+// reads the job's first chunk (`safe` / `ssafe` for an invalid job) and its value is
+// never used (rows past the job, chunks past the row and invalid jobs are skipped
+// where the registers are consumed).  A fixed number of loads per call lets the
+// compiler wait for exactly the loads a computation needs while the next job's are in
+// flight; with conditional loads it would wait for every load issued before the use.
 template <int WK, int LPR, int NC, int RPW, bool TWO>
 __device__ __forceinline__ void load_rows(const Job &jb, int wave, int seg, int sl, uint4 (&w0)[RPW][NC],
                                           uint4 (&w1)[RPW][NC], float (&s0)[RPW][NC],
-                                          float (&s1)[RPW][NC]) {
+                                          float (&s1)[RPW][NC], const uint8_t *safe, const uint16_t *ssafe) {
     constexpr int RPI = 64 / LPR;
     constexpr int RPWG = kWaves * RPW * RPI;
     const size_t rb = row_bytes<WK>(jb.K);
@@ -185,12 +192,13 @@ __device__ __forceinline__ void load_rows(const Job &jb, int wave, int seg, int 
         for (int n = 0; n < NC; ++n) {
             const int c = sl + LPR * n;
             const bool ok = jb.valid && r < jb.rows && c < nch;
-            w0[i][n] = ok ? ld16(jb.W0 + (size_t)r * rb + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
-            if constexpr (TWO)
-                w1[i][n] = ok ? ld16(jb.W1 + (size_t)r * rb + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
+            const size_t off = ok ? (size_t)r * rb + 16 * (size_t)c : 0;
+            w0[i][n] = ld16(jb.valid ? jb.W0 + off : safe);
+            if constexpr (TWO) w1[i][n] = ld16(jb.valid ? jb.W1 + off : safe);
             if constexpr (WK == W_Q4) {
-                s0[i][n] = ok ? f16_to_f32(jb.S0[(size_t)r * nsb + c]) : 0.f;
-                if constexpr (TWO) s1[i][n] = ok ? f16_to_f32(jb.S1[(size_t)r * nsb + c]) : 0.f;
+                const size_t so = ok ? (size_t)r * nsb + c : 0;
+                s0[i][n] = f16_to_f32(*(jb.valid ? jb.S0 + so : ssafe));
+                if constexpr (TWO) s1[i][n] = f16_to_f32(*(jb.valid ? jb.S1 + so : ssafe));
             }
         }
     }
@@ -250,7 +258,12 @@ __host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int s
     return stage_x_bytes(toks, H, xbytes) + (sums ? (((size_t)toks * (H / 32) * 4 + 15) & ~(size_t)15) : 0);
 }
 
-template <int WK, int LPR, int NC>
+// RH: the workgroups rank and bucket the batch themselves (the job records then live
+// in LDS; else in memory, written by a routing launch).  A compile-time choice, so
+// that every record read has one known address space (a read through a pointer that
+// may point to either is a flat load, which makes every later wait a wait for all
+// outstanding memory operations).
+template <int WK, int LPR, int NC, bool RH>
 __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     constexpr int RPW = WTraits<WK>::rpw_gu;
     constexpr int RPI = 64 / LPR;
@@ -298,7 +311,19 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     float asg[RPW][NC], asu[RPW][NC], bsg[RPW][NC], bsu[RPW][NC];
     Job ja{}, jb{};
     bool loaded = false;
-    const bool route_here = p.routed && p.route_here;
+    constexpr bool route_here = RH;
+    // Loads go out in the order their data is needed (memory returns them in issue
+    // order): the batch's logits rows when routing here (at most 8 tokens x 516 floats:
+    // 5 chunks per thread), then the tokens resident in the stage (at most kStageBytes:
+    // 8 chunks per thread), then the first job's weights.  The logits reach LDS as soon
+    // as they arrive, the tokens wait in registers through the routing.
+    constexpr int kLgPre = 5, kXPre = 8;
+    const int n16lg = route_here ? T * logit_stride(p.E) / 4 : 0;
+    uint4 lgpre[kLgPre];
+    load_chunks<kLgPre>(lgpre, n16lg, tid, [&](int i) { return reinterpret_cast<const uint8_t *>(p.logits) + 16 * (size_t)i; });
+    const int n16 = p.x_resident ? (int)(T * xrow / 16) : 0;
+    uint4 xpre[kXPre];
+    load_chunks<kXPre>(xpre, n16, tid, [&](int i) { return (const uint8_t *)p.x + 16 * (size_t)i; });
     if (!route_here) {
         nu = p.routed ? *p.n_unique : 0;
         nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
@@ -306,34 +331,24 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     }
     if (!route_here || j < p.tiles_shared) {  // a shared-expert job needs no routing
         ja = decode(j);
-        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
         loaded = true;
-    }
-    // tokens to stage: with in-kernel routing their loads go out before it, so that
-    // they arrive while the batch is ranked (up to 4 chunks per thread)
-    constexpr int kXPre = 4;
-    const int n16 = p.x_resident ? (int)(T * xrow / 16) : 0;
-    const bool x_early = route_here && n16 <= kXPre * 256;
-    uint4 xpre[kXPre];
-#pragma unroll
-    for (int q = 0; q < kXPre; ++q) xpre[q] = make_uint4(0, 0, 0, 0);
-    if (x_early) {
-#pragma unroll
-        for (int q = 0; q < kXPre; ++q) {
-            const int i = tid + 256 * q;
-            if (i < n16) xpre[q] = ld16((const uint8_t *)p.x + 16 * (size_t)i);
-        }
     }
     if (route_here) {
         // every workgroup ranks and buckets the whole batch; workgroup 0 publishes
         uint8_t *area = lds + p.route_lds_off;
         const RouteLds L = route_lds_layout(T, k, p.E, true);
+        float *lgt = reinterpret_cast<float *>(area + L.lgt);
+#pragma unroll
+        for (int q = 0; q < kLgPre; ++q)
+            if (tid + 256 * q < n16lg) reinterpret_cast<uint4 *>(lgt)[tid + 256 * q] = lgpre[q];
+        lds_barrier();
         const bool pub = blockIdx.x == 0;
         RouteGlobal g{};
         if (pub) g = RouteGlobal{p.ids, p.wts, p.gate_s, const_cast<int *>(p.records),
                                  const_cast<int *>(p.n_unique), const_cast<int *>(p.pairs), p.pos_expert,
                                  p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
-        rank_tokens(p.logits, 0, T, p.E, k, area, L, g, false);
+        rank_tokens(lgt, 0, T, p.E, k, area, L, g, false);
         nu = bucket_tokens(T, k, p.E, area, L, g);
         nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
         recs = reinterpret_cast<const int *>(area + L.records);
@@ -343,36 +358,28 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     if (j >= J) return;
     if (!loaded) {
         ja = decode(j);
-        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+        load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
     }
-    // tokens staged once, their loads in flight together with the first job's weights
-    if (x_early) {
+    // tokens staged once (the stage holds the batch) or per pass inside each job
+    if (p.x_resident) {
 #pragma unroll
-        for (int q = 0; q < kXPre; ++q) {
-            const int i = tid + 256 * q;
-            stage_store(i, xpre[q], i < n16);
-        }
-        __syncthreads();
-    } else if (p.x_resident) {
-        // rounds of 4 chunks per thread (all loads of a round in flight together)
-        for (int b = 0; b < n16; b += 1024) {
-            uint4 xv[4];
-            load_chunks<4>(xv, n16 - b, tid, [&](int i) { return (const uint8_t *)p.x + 16 * (size_t)(b + i); });
-#pragma unroll
-            for (int q = 0; q < 4; ++q) stage_store(b + tid + 256 * q, xv[q], b + tid + 256 * q < n16);
-        }
+        for (int q = 0; q < kXPre; ++q) stage_store(tid + 256 * q, xpre[q], tid + 256 * q < n16);
         __syncthreads();
     }
 
-    auto run = [&](const Job job, const uint4 (&wg)[RPW][NC], const uint4 (&wu)[RPW][NC],
+    // one job's tokens; RES: the stage holds the whole batch (no memory access or barrier
+    // in here, so the next job's loads stay in flight while this job computes), else
+    // the job's tokens are staged pass by pass
+    auto run = [&](auto res, const Job job, const uint4 (&wg)[RPW][NC], const uint4 (&wu)[RPW][NC],
                    const float (&sg)[RPW][NC], const float (&su)[RPW][NC]) {
+        constexpr bool RES = decltype(res)::value;
         if (!job.valid) return;
         float *hout = reinterpret_cast<float *>(job.routed ? (uintptr_t)p.h : (uintptr_t)p.hs);
         const int hstride = job.routed ? p.I : p.Is;
-        const int tpp = p.x_resident ? job.ntok : p.tok_per_pass;
+        const int tpp = RES ? job.ntok : p.tok_per_pass;
         for (int t0 = 0; t0 < job.ntok; t0 += tpp) {
             const int nt = min(tpp, job.ntok - t0);
-            if (!p.x_resident) {
+            if constexpr (!RES) {
                 __syncthreads();
                 // rounds of 4 chunks per thread (all loads of a round in flight together)
                 const int xr16 = (int)(xrow / 16), n16p = nt * xr16;
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                     tok = orow / k;
                 }
                 const bool ook = orow >= 0 && orow < (job.routed ? npairs : T);
-                const size_t srow = p.x_resident ? (size_t)(ook ? tok : 0) : (size_t)a;
+                const size_t srow = RES ? (size_t)(ook ? tok : 0) : (size_t)a;
                 const uint8_t *xr = lds + srow * xrow;
                 float g[RPW], u[RPW];
                 gate_up_token<WK, LPR, NC, RPW>(xr, xbias + srow * nblk, n_chunks, sl, wg, wu, sg, su, g, u);
@@ -415,23 +422,26 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         }
     };
 
-    // two jobs per iteration, registers ping-pong between the A and B sets
-    for (;;) {
-        const int j2 = j + gridDim.x;
-        if (j2 < J) {
+    // two jobs per iteration, registers ping-pong between the A and B sets: the next
+    // job's loads go out before the current job computes, and the last job of the
+    // workgroup runs in a branch of its own, so on every path the compiler knows how
+    // many loads are in flight and a job waits only for its own
+    auto loop = [&](auto res) {
+        for (;;) {
+            const int j2 = j + gridDim.x;
+            if (j2 >= J) { run(res, ja, ag, au, asg, asu); break; }
             jb = decode(j2);
-            load_rows<WK, LPR, NC, RPW, true>(jb, wave, seg, sl, bg, bu, bsg, bsu);
-        }
-        run(ja, ag, au, asg, asu);
-        if (j2 >= J) break;
-        j = j2 + gridDim.x;
-        if (j < J) {
+            load_rows<WK, LPR, NC, RPW, true>(jb, wave, seg, sl, bg, bu, bsg, bsu, p.swg, p.ssg);
+            run(res, ja, ag, au, asg, asu);
+            j = j2 + gridDim.x;
+            if (j >= J) { run(res, jb, bg, bu, bsg, bsu); break; }
             ja = decode(j);
-            load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu);
+            load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
+            run(res, jb, bg, bu, bsg, bsu);
         }
-        run(jb, bg, bu, bsg, bsu);
-        if (j >= J) break;
-    }
+    };
+    if (p.x_resident) loop(std::true_type{});
+    else loop(std::false_type{});
 }
 
 // ---- down: y = down . h per pair, S = shared down . h_s -----------------------------------
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
     uint4 aw[RPW][NC], bw[RPW][NC], dummy[RPW][NC];
     float as[RPW][NC], bs[RPW][NC], dsc[RPW][NC];
     Job ja = decode(j), jb{};
-    load_rows<WK, LPR, NC, RPW, false>(ja, wave, seg, sl, aw, dummy, as, dsc);
+    load_rows<WK, LPR, NC, RPW, false>(ja, wave, seg, sl, aw, dummy, as, dsc, p.swd, p.ssd);
 
     auto run = [&](const Job job, const uint4 (&w)[RPW][NC], const float (&s)[RPW][NC]) {
         if (!job.valid) return;
@@ -541,19 +551,15 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
     };
     for (;;) {
         const int j2 = j + gridDim.x;
-        if (j2 < J) {
-            jb = decode(j2);
-            load_rows<WK, LPR, NC, RPW, false>(jb, wave, seg, sl, bw, dummy, bs, dsc);
-        }
+        if (j2 >= J) { run(ja, aw, as); break; }
+        jb = decode(j2);
+        load_rows<WK, LPR, NC, RPW, false>(jb, wave, seg, sl, bw, dummy, bs, dsc, p.swd, p.ssd);
         run(ja, aw, as);
-        if (j2 >= J) break;
         j = j2 + gridDim.x;
-        if (j < J) {
-            ja = decode(j);
-            load_rows<WK, LPR, NC, RPW, false>(ja, wave, seg, sl, aw, dummy, as, dsc);
-        }
+        if (j >= J) { run(jb, bw, bs); break; }
+        ja = decode(j);
+        load_rows<WK, LPR, NC, RPW, false>(ja, wave, seg, sl, aw, dummy, as, dsc, p.swd, p.ssd);
         run(jb, bw, bs);
-        if (j >= J) break;
     }
 }
 
@@ -730,12 +736,17 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
     if (grid <= 0) return hipSuccess;
     const size_t lds = gate_up_lds_bytes(p, wkind == W_F32 ? 4 : 2);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
-#define GU_LAUNCH(L, N)                                                                          \
-    if (wkind == W_F32) launch_kernel(k_gate_up<W_F32, L, N>, dim3(grid), dim3(256), lds, s, p); \
-    else if (wkind == W_BF16) launch_kernel(k_gate_up<W_BF16, L, N>, dim3(grid), dim3(256), lds, s, p); \
-    else launch_kernel(k_gate_up<W_Q4, L, N>, dim3(grid), dim3(256), lds, s, p);
+    const bool rh = p.routed && p.route_here;
+#define GU_LAUNCH_RH(L, N, RH)                                                                               \
+    if (wkind == W_F32) launch_kernel(k_gate_up<W_F32, L, N, RH>, dim3(grid), dim3(256), lds, s, p);         \
+    else if (wkind == W_BF16) launch_kernel(k_gate_up<W_BF16, L, N, RH>, dim3(grid), dim3(256), lds, s, p);  \
+    else launch_kernel(k_gate_up<W_Q4, L, N, RH>, dim3(grid), dim3(256), lds, s, p);
+#define GU_LAUNCH(L, N)              \
+    if (rh) { GU_LAUNCH_RH(L, N, true) } \
+    else { GU_LAUNCH_RH(L, N, false) }
     MOE_ROWMAP_CASES(GU_LAUNCH)
 #undef GU_LAUNCH
+#undef GU_LAUNCH_RH
     return hipGetLastError();
 }
 
@@ -790,9 +801,9 @@ int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds
     hipError_t e = hipErrorInvalidValue;
 #define OCC_CASE(L, N)                                                                            \
     if (gate_up) {                                                                                \
-        if (wkind == W_F32) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_F32, L, N>, 256, lds); \
-        else if (wkind == W_BF16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, L, N>, 256, lds); \
-        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_Q4, L, N>, 256, lds); \
+        if (wkind == W_F32) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_F32, L, N, true>, 256, lds); \
+        else if (wkind == W_BF16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, L, N, true>, 256, lds); \
+        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_Q4, L, N, true>, 256, lds); \
     } else {                                                                                      \
         if (wkind == W_F32) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_down<W_F32, L, N>, 256, lds); \
         else if (wkind == W_BF16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_down<W_BF16, L, N>, 256, lds); \

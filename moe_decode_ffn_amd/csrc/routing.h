@@ -310,9 +310,13 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
 // local tables the job records, weights and gates also live in LDS (a
 // workgroup that routes for its own use); without, they only go to memory.
 struct RouteLds {
-    size_t ids, pairs, pose, nu, slots, records, scratch, w, g, bytes;
+    size_t ids, pairs, pose, nu, slots, records, scratch, w, g, lgt, bytes;
     bool local;
 };
+
+// A local routing workgroup (the gate/up launch) ranks from a copy of the batch's
+// logits rows in LDS (its lgt region), loaded with one memory round trip ahead of
+// every other load of the workgroup.
 
 __host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, bool local) {
     const size_t np = (size_t)T * k, ns = (size_t)(E < T * k ? E : T * k);
@@ -332,6 +336,8 @@ __host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, bool l
         L.w = o;       o += np * 4;
         L.g = o;       o += (size_t)T * 4;
     }
+    o = (o + 15) & ~(size_t)15;
+    L.lgt = o;     o += local ? (size_t)T * logit_stride(E) * 4 : 0;
     L.bytes = (o + 15) & ~(size_t)15;
     return L;
 }
@@ -350,7 +356,8 @@ struct RouteGlobal {
 };
 
 // Ranks tokens [t_lo, t_hi) (waves take them in turn) into the LDS ids; weights and
-// gates go to g when g.wts is set, else to LDS.  No barrier inside.
+// gates go to g when g.wts is set, else to LDS.  logits: row 0 of the [T][stride]
+// table, in memory or in LDS.  No barrier inside.
 __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int E, int k, uint8_t *area,
                                    const RouteLds &L, const RouteGlobal &g, bool ids_to_global) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
