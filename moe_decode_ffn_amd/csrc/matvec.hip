@@ -52,9 +52,12 @@ __device__ __forceinline__ size_t row_bytes(int k) {
     return WK == W_F32 ? (size_t)k * 4 : WK == W_BF16 ? (size_t)k * 2 : (size_t)k / 2;
 }
 
-// pair id of the a-th token of a routed job (inline in the record up to kRecPairs)
+// pair id of the a-th token of a routed job: inline in a 16-int job record up to
+// kRecPairs (INL), else from the bucketed pairs at the job's first position
+template <bool INL>
 __device__ __forceinline__ int job_pair(const int *rec, const int *pairs, int a) {
-    return a < kRecPairs ? rec[4 + a] : pairs[rec[1] + a];
+    if constexpr (INL) return a < kRecPairs ? rec[4 + a] : pairs[rec[1] + a];
+    return pairs[rec[1] + a];
 }
 
 // ---- chunk dot products ------------------------------------------------------------------
@@ -134,8 +137,10 @@ struct Job {
     const int *rec;           // routed: the job record
 };
 
-// Job j of a launch: shared tiles first, then tiles of used routed experts.
-template <int WK>
+// Job j of a launch: shared tiles first, then tiles of used routed experts.  A used
+// expert's entry in `records` is RI ints: (expert, first position, count, ...) -- a
+// 16-int job record in memory, or a 4-int bucket slot in LDS.
+template <int WK, int RI = kRecInts>
 __device__ __forceinline__ Job decode_job(int j, int tiles_shared, int tiles_routed, int nu,
                                           const int *records, int E, int npairs,
                                           const uint8_t *rW0, const uint8_t *rW1,
@@ -154,7 +159,7 @@ __device__ __forceinline__ Job decode_job(int j, int tiles_shared, int tiles_rou
     j -= tiles_shared;
     const int slot = j / tiles_routed;
     if (slot >= nu) return jb;
-    const int *rec = records + (size_t)slot * kRecInts;
+    const int *rec = records + (size_t)slot * RI;
     const int e = rec[0], start = rec[1], cnt = rec[2];
     if (e < 0 || e >= E || start < 0 || cnt <= 0 || start + cnt > npairs) return jb;
     jb.valid = true; jb.routed = true;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     int nu = 0;
     int j = blockIdx.x;
     auto decode = [&](int jj) {
-        return decode_job<WK>(jj, p.tiles_shared, p.tiles_routed, nu, recs, p.E, npairs, p.wg, p.wu,
+        return decode_job<WK, RH ? 4 : kRecInts>(jj, p.tiles_shared, p.tiles_routed, nu, recs, p.E, npairs, p.wg, p.wu,
                               p.sg, p.su, p.I, H, p.swg, p.swu, p.ssg, p.ssu, p.Is, H, T);
     };
     uint4 ag[RPW][NC], au[RPW][NC], bg[RPW][NC], bu[RPW][NC];
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         rank_tokens(lgt, 0, T, p.E, k, area, L, g, false);
         nu = bucket_tokens(T, k, p.E, area, L, g);
         nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
-        recs = reinterpret_cast<const int *>(area + L.records);
+        recs = reinterpret_cast<const int *>(area + L.slots);  // 4-int bucket slots
         prs = reinterpret_cast<const int *>(area + L.pairs);
     }
     const int J = p.tiles_shared + nu * p.tiles_routed;
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                     const int a = i / xr16, c = i - a * xr16;
                     int tok = t0 + a;
                     if (job.routed) {
-                        const int pr = job_pair(job.rec, prs, t0 + a);
+                        const int pr = job_pair<!RH>(job.rec, prs, t0 + a);
                         tok = (pr >= 0 && pr < npairs) ? pr / k : 0;
                     }
                     return (const uint8_t *)p.x + (size_t)tok * xrow + 16 * (size_t)c;
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
             for (int a = 0; a < nt; ++a) {
                 int orow = t0 + a, tok = t0 + a;
                 if (job.routed) {
-                    orow = job_pair(job.rec, prs, t0 + a);
+                    orow = job_pair<!RH>(job.rec, prs, t0 + a);
                     tok = orow / k;
                 }
                 const bool ook = orow >= 0 && orow < (job.routed ? npairs : T);
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
         for (int a = 0; a < job.ntok; ++a) {
             int orow = a;  // shared: token a
             if (job.routed) {
-                orow = job_pair(job.rec, p.pairs, a);
+                orow = job_pair<true>(job.rec, p.pairs, a);
                 if (orow < 0 || orow >= npairs) continue;
             }
             // plain integer selects (a pointer select here becomes a table in scratch)
@@ -609,46 +614,67 @@ __global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
     for (int i = tid; i < T; i += blockDim.x) s_g[i] = p.gate_s[i];
     __syncthreads();
 
-    for (int u = wave; u < NU; u += kDJWaves) {
+    // a unit's loads: every one issued (a row or chunk that does not exist reads the
+    // unit's first chunk, an invalid unit the shared matrix; such values are never
+    // used), so that with the next unit's loads in flight the current unit waits only
+    // for its own
+    struct Unit {
+        uint4 w[RPW][NC];
+        float sc[RPW][NC];
+        ActChunks<WK, NC> ac;
+        int slot, nch;
+        bool ok;
+    };
+    auto load_unit = [&](int u, Unit &U) {
         const uint8_t *W;
         const uint16_t *Sc = nullptr;
         const float *act;
-        int K, slot;
-        bool ok = true;
+        int K;
+        U.ok = true;
         if (u < NP) {
             const int e = s_pose[u], pr = s_pairs[u];
-            ok = e >= 0 && e < E && pr >= 0 && pr < NP;
-            const size_t m0 = (size_t)(ok ? e : 0) * H;
+            U.ok = e >= 0 && e < E && pr >= 0 && pr < NP;
+            const size_t m0 = (size_t)(U.ok ? e : 0) * H;
             W = p.wd + m0 * row_bytes<WK>(p.I);
             if constexpr (WK == W_Q4) Sc = p.sd + m0 * (p.I / 32);
-            act = p.h + (size_t)(ok ? pr : 0) * p.I;
+            act = p.h + (size_t)(U.ok ? pr : 0) * p.I;
             K = p.I;
-            slot = ok ? pr : 0;
+            U.slot = U.ok ? pr : 0;
         } else {
             const int t = u - NP;
             W = p.swd;
             if constexpr (WK == W_Q4) Sc = p.ssd;
             act = p.hs + (size_t)t * p.Is;
             K = p.Is;
-            slot = NP + t;
+            U.slot = NP + t;
         }
         const size_t rb = row_bytes<WK>(K);
         const int nch = (int)(rb / 16), nsb = K / 32;
-        uint4 w[RPW][NC];
-        float sc[RPW][NC];
+        U.nch = U.ok ? nch : 0;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int r = r0 + i * RPI + seg;
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
                 const int c = sl + LPR * n;
-                const bool v = ok && r < H && c < nch;
-                w[i][n] = v ? ld16(W + (size_t)r * rb + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
-                if constexpr (WK == W_Q4) sc[i][n] = v ? f16_to_f32(Sc[(size_t)r * nsb + c]) : 0.f;
+                const bool v = U.ok && r < H && c < nch;
+                U.w[i][n] = ld16(W + (v ? (size_t)r * rb + 16 * (size_t)c : 0));
+                if constexpr (WK == W_Q4) U.sc[i][n] = f16_to_f32(Sc[v ? (size_t)r * nsb + c : 0]);
             }
         }
-        ActChunks<WK, NC> ac;
-        load_act<WK, LPR, NC>(act, ok ? nch : 0, sl, ac);
+        constexpr int EPC = WTraits<WK>::epc;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const int c = sl + LPR * n;
+            const float *a = act + (c < nch ? EPC * c : 0);
+#pragma unroll
+            for (int q = 0; q < EPC; q += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(a + q);
+                U.ac.v[n][q] = f.x; U.ac.v[n][q + 1] = f.y; U.ac.v[n][q + 2] = f.z; U.ac.v[n][q + 3] = f.w;
+            }
+        }
+    };
+    auto compute_unit = [&](const Unit &U) {
         float asum[NC];
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
@@ -656,13 +682,37 @@ __global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
             if constexpr (WK == W_Q4) {
 #pragma unroll
                 for (int q = 0; q < 32; q += 4)
-                    asum[n] += (ac.v[n][q] + ac.v[n][q + 1]) + (ac.v[n][q + 2] + ac.v[n][q + 3]);
+                    asum[n] += (U.ac.v[n][q] + U.ac.v[n][q + 1]) + (U.ac.v[n][q + 2] + U.ac.v[n][q + 3]);
             }
         }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const float v = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(ac, asum, nch, sl, w, sc, i));
-            if (sl == 0 && ok) s_y[slot * RT + i * RPI + seg] = v;
+            const float v = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(U.ac, asum, U.nch, sl, U.w, U.sc, i));
+            if (sl == 0 && U.ok) s_y[U.slot * RT + i * RPI + seg] = v;
+        }
+    };
+    // units in turn per wave, two register sets ping-ponging where a unit's registers are
+    // few; the wave's last unit runs in a branch of its own (no load after it)
+    constexpr bool DB = RPW * NC * 4 + WTraits<WK>::epc * NC + (WK == W_Q4 ? RPW * NC : 0) <= 48;
+    int u = wave;
+    if constexpr (!DB) {
+        for (; u < NU; u += kDJWaves) {
+            Unit A;
+            load_unit(u, A);
+            compute_unit(A);
+        }
+    } else if (u < NU) {
+        Unit A, B;
+        load_unit(u, A);
+        for (;;) {
+            const int u2 = u + kDJWaves;
+            if (u2 >= NU) { compute_unit(A); break; }
+            load_unit(u2, B);
+            compute_unit(A);
+            u = u2 + kDJWaves;
+            if (u >= NU) { compute_unit(B); break; }
+            load_unit(u, A);
+            compute_unit(B);
         }
     }
     __syncthreads();

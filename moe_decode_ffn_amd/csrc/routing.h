@@ -307,10 +307,11 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
 // ---- one workgroup routes a whole batch ------------------------------------------------
 
 // LDS layout of the routing work area (byte offsets from its start).  With
-// local tables the job records, weights and gates also live in LDS (a
-// workgroup that routes for its own use); without, they only go to memory.
+// local tables the weights, gates and a copy of the batch's logits also live in LDS
+// (a workgroup that routes for its own use, reading its jobs from the bucket slots);
+// without, they only go to memory.  Job records only ever go to memory.
 struct RouteLds {
-    size_t ids, pairs, pose, nu, slots, records, scratch, w, g, lgt, bytes;
+    size_t ids, pairs, pose, nu, slots, scratch, w, g, lgt, bytes;
     bool local;
 };
 
@@ -332,7 +333,6 @@ __host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, bool l
     L.scratch = o; o += (size_t)bucket_scratch_ints(E, T) * 4;
     o = (o + 15) & ~(size_t)15;
     if (local) {
-        L.records = o; o += ns * kRecInts * 4;
         L.w = o;       o += np * 4;
         L.g = o;       o += (size_t)T * 4;
     }
@@ -374,10 +374,11 @@ __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int 
     }
 }
 
-// With every id in LDS: buckets the pairs and builds the job records in LDS
+// With every id in LDS: buckets the pairs into the LDS slots and pairs
 // (expert-ascending buckets; a single token's buckets follow its rank order);
-// copies the tables to g where its pointers are set.  Barriers inside: call
-// from every thread of the workgroup.  Returns the used-expert count.
+// builds the job records in g.records and copies the tables to g where its
+// pointers are set.  Barriers inside: call from every thread of the workgroup.
+// Returns the used-expert count.
 __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const RouteLds &L,
                                     const RouteGlobal &g) {
     const int tid = threadIdx.x, NP = T * k;
@@ -386,7 +387,6 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
     int *pose = reinterpret_cast<int *>(area + L.pose);
     int *nup = reinterpret_cast<int *>(area + L.nu);
     int4 *slots = reinterpret_cast<int4 *>(area + L.slots);
-    int *rec = reinterpret_cast<int *>(area + L.records);
     lds_barrier();
     if (T == 1) {  // one token: its k picks are k distinct experts, one bucket each, in rank order
         if (threadIdx.x < 64) {
@@ -406,7 +406,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
     }
     lds_barrier();
     const int nu = *nup;
-    for (int i = tid; i < nu * kRecInts; i += blockDim.x) {
+    for (int i = tid; g.records && i < nu * kRecInts; i += blockDim.x) {
         const int u = i / kRecInts, f = i - u * kRecInts;
         const int4 sv = slots[u];
         int v;
@@ -415,8 +415,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
         else if (f == 2) v = sv.z;
         else if (f == 3) v = 0;
         else v = (f - 4 < sv.z) ? pairs[sv.y + f - 4] : -1;
-        if (L.local) rec[i] = v;
-        if (g.records) g.records[i] = v;
+        g.records[i] = v;
     }
     if (g.ids)
         for (int i = tid; i < NP; i += blockDim.x) {
