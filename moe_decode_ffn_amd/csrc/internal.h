@@ -19,7 +19,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxDim = 8192;
 constexpr int kDefaultMatvecMax = 16;  // measured crossover of the mat-vec and grouped-GEMM kernels
-constexpr int kRouteInGateUpMax = 8;  // up to this batch the gate/up workgroups route it themselves
+constexpr int kRouteInGateUpMax = 16;  // up to this batch the gate/up workgroups route it themselves
 constexpr int kRouteKernelMax = 16;   // up to this batch k_route routes it (else the batch launches)
 constexpr int kPfMinBucket = 32;      // mean tokens per used expert from which the prefill GEMM runs
 constexpr size_t kWsAlign = 256;

@@ -30,9 +30,12 @@ SMALL = {
     "bf16_k_equals_e": (synth.LayerShape(64, 4, 4, 32, 32, "bf16", "bf16"), 9, (3,)),
     "bf16_one_expert": (synth.LayerShape(96, 1, 1, 64, 32, "bf16", "bf16"), 10, (2,)),
     "q4_wide": (synth.LayerShape(1024, 16, 4, 256, 128, "bf16", "q4"), 11, (1, 6)),
-    # top-16: 48 pairs (one-wave sort), 96 pairs in the gate/up workgroups and 192 in
-    # the routing launch (workgroup bucketing)
+    # top-16: 48 pairs (one-wave sort), 96 and 192 pairs in the gate/up workgroups
+    # (workgroup bucketing)
     "bf16_top16": (synth.LayerShape(128, 24, 16, 64, 32, "bf16", "bf16"), 12, (3, 6, 12)),
+    # 512 experts: 2 tokens route in the gate/up workgroups; 12 tokens' logits rows exceed
+    # what their prologue holds, so the routing launch of its own ranks them
+    "bf16_512_experts": (synth.LayerShape(128, 512, 8, 64, 32, "bf16", "bf16"), 13, (2, 12)),
 }
 
 
@@ -117,8 +120,9 @@ def _decode_layer(shape, seed):
 FULL = {
     # name: (shape, seed, tokens, regime flags); the default regime switches to the
     # grouped GEMM above 16 tokens for bf16, so both regimes are also forced at
-    # batches on the other side of it; routing runs in the gate/up launch up to 8
-    # tokens, in its own launch up to 16 and in the batch launches above
+    # batches on the other side of it; routing runs in the gate/up launch up to 16
+    # tokens (in its own launch where the batch's logits rows do not fit the gate/up
+    # prologue) and in the batch launches above
     "decode_bf16_t1": (synth.DECODE_BF16, 1, 1, 0),
     "decode_bf16_t4": (synth.DECODE_BF16, 2, 4, 0),
     "decode_bf16_t5": (synth.DECODE_BF16, 2, 5, 0),
