@@ -65,8 +65,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU split of the layer is a "
-              "design (see DESIGN.md), not a measured path", file=sys.stderr)
+        print("bench.py: the layer runs on one GPU only; splitting it over several GPUs "
+              "(experts or their rows sharded per GPU) is described, not implemented", file=sys.stderr)
         return 2
 
     import numpy as np
