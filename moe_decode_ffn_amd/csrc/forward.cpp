@@ -99,6 +99,7 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
     if ((e = hipDeviceGetAttribute(&P->cu_count, hipDeviceAttributeMultiprocessorCount, P->d.device)) != hipSuccess)
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
+    P->occ_gu1 = P->map_gu.lpr == 64 ? gate_up_one_row_occupancy(P->map_gu, kStageBytes) : 1;
     P->occ_d = expert_kernel_occupancy(false, P->wkind, P->map_down, 0);
     if (P->gemm_ok) {
         for (int i = 0; i < 3; ++i) {
@@ -269,9 +270,6 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     // bucketing launches of their own, through global memory
     const bool batch_route = !gp.route_here && !route_kernel;
     rp.bcount = batch_route ? (int *)(W + L.bcount) : nullptr;
-    const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu);
-    gp.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
-    const int gu_tiles_s = (int)((Is + gu_rows - 1) / gu_rows);
     const int max_used = (int)std::min(E, T * k);
 
     DownParams dp{};
@@ -343,11 +341,15 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     auto run_gate_up = [&](hipStream_t s, bool routed, bool shared) {
         GateUpParams g = gp;
         g.routed = routed ? 1 : 0;
-        g.tiles_shared = shared ? gu_tiles_s : 0;
+        // rows per job depend on the kernel this launch takes (routing here or not)
+        const bool one_row = gate_up_one_row(wk, P->map_gu, Ti, routed && g.route_here);
+        const int gu_rows = gate_up_rows_per_wg(wk, P->map_gu, Ti, routed && g.route_here);
+        g.tiles_routed = (int)((I + gu_rows - 1) / gu_rows);
+        g.tiles_shared = shared ? (int)((Is + gu_rows - 1) / gu_rows) : 0;
         const int jobs = g.tiles_shared + (routed ? max_used * g.tiles_routed : 0);
         const int kid = routed ? MOE_FFN_K_GATE_UP : MOE_FFN_K_SH_GATE_UP;
         return timed(P, kid, s, [&] {
-            return launch_gate_up(g, wk, P->map_gu, expert_grid(jobs, P->occ_gu), s);
+            return launch_gate_up(g, wk, P->map_gu, expert_grid(jobs, one_row ? P->occ_gu1 : P->occ_gu), s);
         });
     };
     auto run_down = [&](hipStream_t s, bool routed, bool shared) {

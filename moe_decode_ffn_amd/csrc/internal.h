@@ -89,6 +89,7 @@ struct moe_ffn_plan_s {
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     int cu_count = 0;       // compute units of the device
     int occ_gu = 0, occ_d = 0;  // resident workgroups per CU of the expert kernels
+    int occ_gu1 = 0;            // the same for the one-row-per-wave gate/up kernel
     int occ_gg_gu[3] = {0, 0, 0}, occ_gg_d[3] = {0, 0, 0};  // grouped GEMM, 16/32/64 tokens per pass
     int occ_pf_gu[3] = {0, 0, 0}, occ_pf_d[3] = {0, 0, 0};  // prefill GEMM, 128/192/256 tokens per pass
     bool gemm_ok = false;   // shapes and storage the grouped GEMM supports
@@ -273,7 +274,9 @@ int gg_rows_per_job();
 hipError_t launch_delay(hipStream_t s, uint64_t ticks);
 
 // rows each workgroup covers for a kernel family and row map
-int gate_up_rows_per_wg(int wkind, const RowMap &m);
+int gate_up_rows_per_wg(int wkind, const RowMap &m, int T, bool route_here);
+bool gate_up_one_row(int wkind, const RowMap &m, int T, bool route_here);
+int gate_up_one_row_occupancy(const RowMap &m, size_t lds);
 int down_rows_per_wg(int wkind, const RowMap &m);
 size_t gate_up_lds_bytes(const GateUpParams &p, int xbytes);
 int gate_up_route_lds_off(const GateUpParams &p, int xbytes);

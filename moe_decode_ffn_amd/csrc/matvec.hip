@@ -44,7 +44,15 @@ static int rpw_d_of(int wk) {
                                                              : WTraits<W_Q4>::rpw_d;
 }
 
-int gate_up_rows_per_wg(int wkind, const RowMap &m) { return kWaves * rpw_gu_of(wkind) * (64 / m.lpr); }
+// A one-token bf16 batch routed inside the gate/up workgroups reads one row per wave per
+// job instead of two: twice the jobs (about two per resident workgroup instead of one and a
+// fraction), so the launch's single round of jobs ends more evenly.
+bool gate_up_one_row(int wkind, const RowMap &m, int T, bool route_here) {
+    return wkind == W_BF16 && m.lpr == 64 && T == 1 && route_here;
+}
+int gate_up_rows_per_wg(int wkind, const RowMap &m, int T, bool route_here) {
+    return kWaves * (gate_up_one_row(wkind, m, T, route_here) ? 1 : rpw_gu_of(wkind)) * (64 / m.lpr);
+}
 int down_rows_per_wg(int wkind, const RowMap &m) { return kWaves * rpw_d_of(wkind) * (64 / m.lpr); }
 
 template <int WK>
@@ -268,9 +276,9 @@ __host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int s
 // that every record read has one known address space (a read through a pointer that
 // may point to either is a flat load, which makes every later wait a wait for all
 // outstanding memory operations).
-template <int WK, int LPR, int NC, bool RH>
+template <int WK, int LPR, int NC, bool RH, int RPWX = 0>
 __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
-    constexpr int RPW = WTraits<WK>::rpw_gu;
+    constexpr int RPW = RPWX ? RPWX : WTraits<WK>::rpw_gu;  // rows per wave per job
     constexpr int RPI = 64 / LPR;
     constexpr int RPWG = kWaves * RPW * RPI;
     constexpr int XB = WK == W_F32 ? 4 : 2;  // bytes per activation element
@@ -787,6 +795,19 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
     const size_t lds = gate_up_lds_bytes(p, wkind == W_F32 ? 4 : 2);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
     const bool rh = p.routed && p.route_here;
+    if (gate_up_one_row(wkind, m, p.T, rh)) {
+#define GU_ONE_ROW(L, N) launch_kernel(k_gate_up<W_BF16, 64, N, true, 1>, dim3(grid), dim3(256), lds, s, p);
+        switch (m.nc) {
+        case 1: GU_ONE_ROW(64, 1); break;
+        case 2: GU_ONE_ROW(64, 2); break;
+        case 4: GU_ONE_ROW(64, 4); break;
+        case 8: GU_ONE_ROW(64, 8); break;
+        case 16: GU_ONE_ROW(64, 16); break;
+        default: return hipErrorInvalidValue;
+        }
+#undef GU_ONE_ROW
+        return hipGetLastError();
+    }
 #define GU_LAUNCH_RH(L, N, RH)                                                                               \
     if (wkind == W_F32) launch_kernel(k_gate_up<W_F32, L, N, RH>, dim3(grid), dim3(256), lds, s, p);         \
     else if (wkind == W_BF16) launch_kernel(k_gate_up<W_BF16, L, N, RH>, dim3(grid), dim3(256), lds, s, p);  \
@@ -871,6 +892,21 @@ int expert_kernel_occupancy(bool gate_up, int wkind, const RowMap &m, size_t lds
     default: break;
     }
 #undef OCC_CASE
+    return e == hipSuccess && n > 0 ? n : 1;
+}
+
+// The same for the one-row-per-wave gate/up kernel (bf16, 64-lane rows).
+int gate_up_one_row_occupancy(const RowMap &m, size_t lds) {
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (m.nc) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, 64, 1, true, 1>, 256, lds); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, 64, 2, true, 1>, 256, lds); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, 64, 4, true, 1>, 256, lds); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, 64, 8, true, 1>, 256, lds); break;
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gate_up<W_BF16, 64, 16, true, 1>, 256, lds); break;
+    default: break;
+    }
     return e == hipSuccess && n > 0 ? n : 1;
 }
 
