@@ -44,11 +44,12 @@ static int rpw_d_of(int wk) {
                                                              : WTraits<W_Q4>::rpw_d;
 }
 
-// A one-token bf16 batch routed inside the gate/up workgroups reads one row per wave per
-// job instead of two: twice the jobs (about two per resident workgroup instead of one and a
-// fraction), so the launch's single round of jobs ends more evenly.
+// A bf16 batch of up to 3 tokens routed inside the gate/up workgroups reads one row per
+// wave per job instead of two: twice the jobs over more resident workgroups, so the last
+// round of jobs is a smaller part of the launch (from 4 tokens on, the two-row jobs, which
+// read each staged token once for two rows, are faster).
 bool gate_up_one_row(int wkind, const RowMap &m, int T, bool route_here) {
-    return wkind == W_BF16 && m.lpr == 64 && T == 1 && route_here;
+    return wkind == W_BF16 && m.lpr == 64 && T <= 3 && route_here;
 }
 int gate_up_rows_per_wg(int wkind, const RowMap &m, int T, bool route_here) {
     return kWaves * (gate_up_one_row(wkind, m, T, route_here) ? 1 : rpw_gu_of(wkind)) * (64 / m.lpr);
