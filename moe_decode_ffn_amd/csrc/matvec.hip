@@ -327,8 +327,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     bool loaded = false;
     constexpr bool route_here = RH;
     // Loads go out in the order their data is needed (memory returns them in issue
-    // order): the batch's logits rows when routing here (at most 8 tokens x 516 floats:
-    // 5 chunks per thread), then the tokens resident in the stage (at most kStageBytes:
+    // order): the batch's logits rows when routing here (at most 5 16-byte chunks per
+    // thread, e.g. 16 tokens of 256 experts), then the tokens resident in the stage (at most kStageBytes:
     // 8 chunks per thread), then the first job's weights.  The logits reach LDS as soon
     // as they arrive, the tokens wait in registers through the routing.
     constexpr int kLgPre = 5, kXPre = 8;
