@@ -25,11 +25,11 @@
  * Ownership: the caller owns every tensor, the workspace and the stream; the
  * library borrows them for the duration of the enqueued work (same page,
  * section "Backend services": borrowed device and stream, ordered with the
- * caller's work).  The plan owns a second HIP stream, two events and about
- * 1 KiB of device memory (arrival counters of the routing step, zero between
- * calls),
- * created lazily by the first forward, which therefore must not run under
- * stream capture.
+ * caller's work).  The plan owns no device memory.  A plan whose shared-expert
+ * mode uses the second stream (MOE_FFN_SHARED_AUX) owns that HIP stream and two
+ * events, created lazily by its first forward; every plan queries the device
+ * (compute units, kernel occupancy) in its first forward, which therefore must
+ * not run under stream capture.
  *
  * Threading: a plan serialises nothing.  Two forwards of one plan must not
  * run concurrently (they share the plan's stream and usually the workspace).
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
 
 typedef enum moe_ffn_status {
     MOE_FFN_OK = 0,
@@ -187,15 +187,46 @@ typedef struct moe_ffn_plan_info {
     uint32_t shared_mode_gemm;   /* ... and above it */
 } moe_ffn_plan_info;
 
+/* Where a forward leaves the routing step's integer tables in the workspace:
+ * byte offsets from the workspace base, each 256-byte aligned.  The bucketing
+ * step groups the batch's (token, slot) pairs by expert so that each selected
+ * expert's weights are streamed once per call, whatever the number of tokens
+ * that chose it (the routed experts of page "ggml-cuda: overlap the MoE shared
+ * expert on a separate stream", section "What this changes", run as mat-vecs
+ * at small batches).  Pair q = t*k + j is slot j (rank order) of token t.
+ * The tables hold the last forward's results once its work on the stream has
+ * completed, until the next call that uses the workspace (page "ggml operator
+ * extensions", section "Kernel selection": workspace contents are not
+ * preserved between calls).  For tests and tools; no forward reads them from
+ * a previous call. */
+typedef struct moe_ffn_routing_layout {
+    size_t ids;           /* int32 [T*k]: expert of pair q, slots in rank order */
+    size_t weights;       /* fp32 [T*k]: renormalised routing weight of pair q */
+    size_t gate;          /* fp32 [T]: sigmoid gate of the shared expert per token */
+    size_t n_used;        /* int32: distinct experts the batch selected (U) */
+    size_t records;       /* int32 [U][record_ints]: one job record per used expert:
+                             (expert, first bucketed position, pair count, 0, then the
+                             first record_pairs pair ids of its bucket, -1 past the count);
+                             experts ascending, except for one token, whose k experts
+                             keep its rank order */
+    size_t pairs;         /* int32 [T*k]: pair ids in bucketed order; each expert's bucket
+                             is contiguous and holds its pairs in ascending order */
+    size_t pair_expert;   /* int32 [T*k]: expert of each bucketed position */
+    int32_t record_ints;  /* ints per job record */
+    int32_t record_pairs; /* pair ids held in a record */
+} moe_ffn_routing_layout;
+
 /* Kernel ids for the profiling hooks. */
 typedef enum moe_ffn_kernel_id {
     MOE_FFN_K_ROUTER = 0,       /* router (logits and the shared-gate logit): a GEMV up to 16 tokens
                                    (and for fp32 tokens or with the input norm), an MFMA GEMM
                                    above */
-    MOE_FFN_K_ROUTE = 1,        /* routing launch (top-k, renormalisation, bucketing) up to 16 tokens,
-                                   except up to 4 tokens in the mat-vec regime, where the routed
-                                   gate/up launch routes; above 16 tokens the ranking launch
-                                   (top-k, renormalisation, per-expert counts) */
+    MOE_FFN_K_ROUTE = 1,        /* routing launch of its own (top-k, renormalisation, bucketing) for
+                                   up to 16 tokens whose routing does not fit the routed gate/up
+                                   launch (which routes batches of up to 16 tokens itself when the
+                                   batch's logits rows and the routing tables fit its LDS); above
+                                   16 tokens the ranking launch (top-k, renormalisation,
+                                   per-expert counts) */
     MOE_FFN_K_GATE_UP = 2,      /* gate/up + SiLU*up (routed, or routed + shared when fused) */
     MOE_FFN_K_DOWN = 3,         /* down per (token, slot) pair (routed, or + shared when fused) */
     MOE_FFN_K_SH_GATE_UP = 4,   /* gate/up of the shared expert alone (either regime) */
@@ -218,7 +249,8 @@ const char *moe_ffn_status_string(int32_t status);
 const char *moe_ffn_last_error(void);
 
 /* sizeof(moe_ffn_desc) for which = 0, sizeof(moe_ffn_tensors) for 1,
- * sizeof(moe_ffn_plan_info) for 2, else 0 (lets bindings check their mirrors). */
+ * sizeof(moe_ffn_plan_info) for 2, sizeof(moe_ffn_routing_layout) for 3, else 0
+ * (lets bindings check their mirrors). */
 size_t moe_ffn_struct_size(int32_t which);
 
 /* Validates desc and creates a plan.  Host only: no HIP call.  On success
@@ -234,6 +266,10 @@ moe_ffn_status moe_ffn_plan(const moe_ffn_desc *desc, moe_ffn_plan_t *out_plan,
 
 /* Copies the plan's decisions into *info. */
 moe_ffn_status moe_ffn_plan_get_info(moe_ffn_plan_t plan, moe_ffn_plan_info *info);
+
+/* Copies the workspace offsets of the routing tables into *layout (host only;
+ * MOE_FFN_ERR_INVALID_ARG for a NULL argument). */
+moe_ffn_status moe_ffn_plan_get_routing_layout(moe_ffn_plan_t plan, moe_ffn_routing_layout *layout);
 
 /* Enqueues the layer for tokens 0 .. n_tokens-1 on `stream` (a hipStream_t of
  * desc.device; NULL is that device's null stream) and returns without

@@ -1,7 +1,7 @@
 """Builds libmoe_ffn.so for gfx950 in-tree (moe_decode_ffn_amd/lib/), and the
 layer_loop driver (a C-ABI-only program for profiler runs) beside it.
 
-    python -m moe_decode_ffn_amd.build
+    python -m moe_decode_ffn_amd.build [--changed]
 
 Every HIP source is compiled with hipcc for gfx950 only, with packed fp32
 instructions disabled (-packed-fp32-ops) and no floating-point contraction
@@ -23,8 +23,6 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBRARY = os.path.join(LIBDIR, "libmoe_ffn.so")
 DRIVER_SRC = os.path.join(PKG, "driver", "layer_loop.hip")
 DRIVER = os.path.join(LIBDIR, "layer_loop")
-BARRIER_SRC = os.path.join(PKG, "driver", "grid_barrier.hip")
-BARRIER = os.path.join(LIBDIR, "grid_barrier")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -39,8 +37,19 @@ def sources() -> list[str]:
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
+def _up_to_date(src: str, obj: str) -> bool:
+    """The object is newer than its source and every header it may include."""
+    if not os.path.exists(obj):
+        return False
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    deps.append(os.path.join(INCLUDE, "moe_ffn.h"))
+    return all(os.path.getmtime(obj) > os.path.getmtime(d) for d in deps)
+
+
+def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    if not force and _up_to_date(src, obj):
+        return obj
     cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,13 +57,15 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int | None = None) -> str:
+def build_library(jobs: int | None = None, force: bool = True) -> str:
+    """Compiles every source (force=False: only those whose object is out of date) and
+    links the library."""
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, force), srcs))
     tmp = LIBRARY + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,24 +76,17 @@ def build_library(jobs: int | None = None) -> str:
 
 
 def build_driver() -> str:
-    """layer_loop, linked against the in-tree library (found next to it at run time), and
-    grid_barrier."""
+    """layer_loop, linked against the in-tree library (found next to it at run time)."""
     tmp = DRIVER + ".tmp"
     cmd = [HIPCC, *COMMON, DRIVER_SRC, "-o", tmp, f"-L{LIBDIR}", "-lmoe_ffn", "-Wl,-rpath,$ORIGIN"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {DRIVER_SRC}:\n{r.stderr}")
     os.replace(tmp, DRIVER)
-    # the grid-barrier cost driver (stand-alone: no library)
-    tmp = BARRIER + ".tmp"
-    r = subprocess.run([HIPCC, *COMMON, BARRIER_SRC, "-o", tmp], capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {BARRIER_SRC}:\n{r.stderr}")
-    os.replace(tmp, BARRIER)
     return DRIVER
 
 
 if __name__ == "__main__":
-    print(build_library())
+    print(build_library(force="--changed" not in sys.argv))
     print(build_driver())
     sys.exit(0)

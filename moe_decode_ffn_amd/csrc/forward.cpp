@@ -3,8 +3,11 @@
 // Kernels of one forward:
 //   router  logits of E router rows and of the shared-gate vector
 //   routing top-k, renormalised weights, bucketing, job records: in every
-//           routed mat-vec gate/up workgroup (up to 4 tokens), in k_route (up
-//           to 32 tokens) or in the router launch's tail (above)
+//           routed mat-vec gate/up workgroup (up to 16 tokens, when the batch's
+//           logits rows and routing tables fit that launch's LDS), else in a
+//           routing launch of its own (k_route, one workgroup, up to 16 tokens),
+//           else in three batch launches (ranking with per-workgroup expert
+//           counts, a per-expert scan of the counts, the placement of the pairs)
 //   gate/up h = silu(gate x) * (up x) for every (token, slot) pair [+ shared]
 //   down    y = down h per pair [+ S for the shared expert]
 //   join    out = sum_j w_j y_j + s * S (mat-vec regime: k_down_join does the
@@ -90,12 +93,15 @@ moe_ffn_status lazy_init(moe_ffn_plan_s *P, hipStream_t stream) {
     if (cs != hipStreamCaptureStatusNone)
         return set_error(MOE_FFN_ERR_UNSUPPORTED,
                          "the first forward of a plan creates its stream and events and must not be captured");
-    if ((e = hipStreamCreateWithFlags(&P->aux, hipStreamNonBlocking)) != hipSuccess)
-        return hip_fail(e, "hipStreamCreateWithFlags");
-    if ((e = hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming)) != hipSuccess)
-        return hip_fail(e, "hipEventCreateWithFlags");
-    if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
-        return hip_fail(e, "hipEventCreateWithFlags");
+    // the second stream and its events exist only for a plan that forks onto it
+    if (P->mode_matvec == MOE_FFN_SHARED_AUX || P->mode_gemm == MOE_FFN_SHARED_AUX) {
+        if ((e = hipStreamCreateWithFlags(&P->aux, hipStreamNonBlocking)) != hipSuccess)
+            return hip_fail(e, "hipStreamCreateWithFlags");
+        if ((e = hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(e, "hipEventCreateWithFlags");
+        if ((e = hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(e, "hipEventCreateWithFlags");
+    }
     if ((e = hipDeviceGetAttribute(&P->cu_count, hipDeviceAttributeMultiprocessorCount, P->d.device)) != hipSuccess)
         return hip_fail(e, "hipDeviceGetAttribute");
     P->occ_gu = expert_kernel_occupancy(true, P->wkind, P->map_gu, kStageBytes);
@@ -249,8 +255,8 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t P, const moe_ffn_tensors *t, int32
     gp.swg = (const uint8_t *)t->sh_gate; gp.swu = (const uint8_t *)t->sh_up;
     gp.ssg = t->sh_gate_scale; gp.ssu = t->sh_up_scale; gp.Is = (int)Is; gp.hs = sh_h;
     // small batches: every routed gate/up workgroup ranks and buckets the batch from
-    // the logits (no routing step between the router and the experts); larger
-    // ones: the router launch's last workgroups do it once
+    // the logits (no routing step between the router and the experts); otherwise a
+    // routing launch of its own (up to 16 tokens) or the batch routing launches
     gp.logits = logits; gp.ids = ids; gp.wts = wts; gp.gate_s = gate_s; gp.pos_expert = pos_expert;
     gp.dbg_ids = t->dbg_topk_ids; gp.dbg_w = t->dbg_topk_weights;
     gp.dbg_logits = t->dbg_logits; gp.dbg_gate = t->dbg_shared_gate;

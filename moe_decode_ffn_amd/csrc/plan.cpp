@@ -77,6 +77,7 @@ size_t moe_ffn_struct_size(int32_t which) {
     case 0: return sizeof(moe_ffn_desc);
     case 1: return sizeof(moe_ffn_tensors);
     case 2: return sizeof(moe_ffn_plan_info);
+    case 3: return sizeof(moe_ffn_routing_layout);
     default: return 0;
     }
 }
@@ -192,6 +193,21 @@ moe_ffn_status moe_ffn_plan_get_info(moe_ffn_plan_t plan, moe_ffn_plan_info *inf
     info->matvec_max_tokens = plan->matvec_max;
     info->shared_mode_matvec = plan->mode_matvec;
     info->shared_mode_gemm = plan->mode_gemm;
+    return MOE_FFN_OK;
+}
+
+moe_ffn_status moe_ffn_plan_get_routing_layout(moe_ffn_plan_t plan, moe_ffn_routing_layout *layout) {
+    if (!plan || !layout) return set_error(MOE_FFN_ERR_INVALID_ARG, "plan and layout must not be NULL");
+    const Layout &L = plan->L;
+    layout->ids = L.ids;
+    layout->weights = L.wts;
+    layout->gate = L.gate_s;
+    layout->n_used = L.n_unique;
+    layout->records = L.records;
+    layout->pairs = L.pairs;
+    layout->pair_expert = L.pos_expert;
+    layout->record_ints = kRecInts;
+    layout->record_pairs = kRecPairs;
     return MOE_FFN_OK;
 }
 

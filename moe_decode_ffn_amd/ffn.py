@@ -14,7 +14,7 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "lib", "libmoe_ffn.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # moe_ffn_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL = 0, 1, 2, 3
@@ -67,6 +67,13 @@ class PlanInfo(ctypes.Structure):
                 ("shared_mode_gemm", ctypes.c_uint32)]
 
 
+class RoutingLayout(ctypes.Structure):
+    _fields_ = [("ids", ctypes.c_size_t), ("weights", ctypes.c_size_t), ("gate", ctypes.c_size_t),
+                ("n_used", ctypes.c_size_t), ("records", ctypes.c_size_t), ("pairs", ctypes.c_size_t),
+                ("pair_expert", ctypes.c_size_t), ("record_ints", ctypes.c_int32),
+                ("record_pairs", ctypes.c_int32)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -89,6 +96,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.moe_ffn_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_ffn_plan_get_info.restype = ctypes.c_int32
     lib.moe_ffn_plan_get_info.argtypes = [_P, ctypes.POINTER(PlanInfo)]
+    lib.moe_ffn_plan_get_routing_layout.restype = ctypes.c_int32
+    lib.moe_ffn_plan_get_routing_layout.argtypes = [_P, ctypes.POINTER(RoutingLayout)]
     lib.moe_ffn_forward.restype = ctypes.c_int32
     lib.moe_ffn_forward.argtypes = [_P, ctypes.POINTER(Tensors), ctypes.c_int32, _P,
                                     ctypes.c_size_t, _P]
@@ -101,7 +110,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_int64)]
     if lib.moe_ffn_abi_version() != ABI_VERSION:
         raise ImportError("libmoe_ffn.so ABI version mismatch")
-    for which, st in enumerate((Desc, Tensors, PlanInfo)):
+    for which, st in enumerate((Desc, Tensors, PlanInfo, RoutingLayout)):
         if lib.moe_ffn_struct_size(which) != ctypes.sizeof(st):
             raise ImportError(f"struct mirror {st.__name__} does not match the library")
     _lib = lib
@@ -135,6 +144,13 @@ def moe_ffn_plan_get_info(plan: int) -> PlanInfo:
     info = PlanInfo()
     _check(load().moe_ffn_plan_get_info(plan, ctypes.byref(info)), "moe_ffn_plan_get_info")
     return info
+
+
+def moe_ffn_plan_get_routing_layout(plan: int) -> RoutingLayout:
+    lay = RoutingLayout()
+    _check(load().moe_ffn_plan_get_routing_layout(plan, ctypes.byref(lay)),
+           "moe_ffn_plan_get_routing_layout")
+    return lay
 
 
 def moe_ffn_forward(plan: int, tensors: Tensors, n_tokens: int, workspace: int,
@@ -196,6 +212,28 @@ class MoeFfn:
 
     def info(self) -> PlanInfo:
         return moe_ffn_plan_get_info(self.plan)
+
+    def routing_layout(self) -> RoutingLayout:
+        return moe_ffn_plan_get_routing_layout(self.plan)
+
+    def routing_tables(self, workspace, n_tokens: int) -> dict:
+        """Views of the routing tables a forward of n_tokens left in `workspace` (a uint8
+        tensor): ids, weights, gate, n_used, records [U, record_ints], pairs, pair_expert."""
+        import torch
+        lay = self.routing_layout()
+        npair = n_tokens * self.desc.top_k
+
+        def view(off, n, dtype):
+            return workspace[off:off + 4 * n].view(dtype)
+
+        n_used = int(view(lay.n_used, 1, torch.int32).item())
+        n_rec = max(0, min(n_used, self.desc.n_experts))
+        return {"ids": view(lay.ids, npair, torch.int32), "weights": view(lay.weights, npair, torch.float32),
+                "gate": view(lay.gate, n_tokens, torch.float32), "n_used": n_used,
+                "records": view(lay.records, n_rec * lay.record_ints, torch.int32).reshape(n_rec, lay.record_ints),
+                "pairs": view(lay.pairs, npair, torch.int32),
+                "pair_expert": view(lay.pair_expert, npair, torch.int32),
+                "record_pairs": lay.record_pairs}
 
     def close(self) -> None:
         if self.plan:

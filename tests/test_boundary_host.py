@@ -56,6 +56,7 @@ def test_abi_version_and_struct_mirrors(lib):
     assert lib.moe_ffn_struct_size(0) == ctypes.sizeof(ffn.Desc)
     assert lib.moe_ffn_struct_size(1) == ctypes.sizeof(ffn.Tensors)
     assert lib.moe_ffn_struct_size(2) == ctypes.sizeof(ffn.PlanInfo)
+    assert lib.moe_ffn_struct_size(3) == ctypes.sizeof(ffn.RoutingLayout)
     assert lib.moe_ffn_struct_size(99) == 0
 
 
@@ -197,6 +198,29 @@ def test_workspace_with_batch_routing(lib, T):
     assert info.routing_region_bytes == routing
     assert ws == info.workspace_bytes == (_align(T * Is * 4) + _align(T * H * 4) + routing
                                           + _align(T * k * I * 4) + _align(T * k * H * 4))
+
+
+@pytest.mark.parametrize("T", [1, 16, 300])
+def test_routing_layout_lies_in_the_routing_region(lib, T):
+    # the routing tables a forward leaves in the workspace: 256-byte aligned, disjoint,
+    # inside the routing region (after the shared branch's region, before the phases)
+    E, k = 256, 8
+    plan, ws = ffn.moe_ffn_plan(desc(max_tokens=T))
+    info = ffn.moe_ffn_plan_get_info(plan)
+    lay = ffn.moe_ffn_plan_get_routing_layout(plan)
+    ffn.moe_ffn_destroy(plan)
+    assert (lay.record_ints, lay.record_pairs) == (16, 12)
+    tables = [(lay.ids, T * k * 4), (lay.weights, T * k * 4), (lay.gate, T * 4), (lay.n_used, 4),
+              (lay.records, E * lay.record_ints * 4), (lay.pairs, T * k * 4), (lay.pair_expert, T * k * 4)]
+    lo, hi = info.shared_region_bytes, info.shared_region_bytes + info.routing_region_bytes
+    for off, n in tables:
+        assert off % 256 == 0 and lo <= off and off + n <= hi
+    spans = sorted(tables)
+    for (a, na), (b, _) in zip(spans, spans[1:]):
+        assert a + na <= b
+    with pytest.raises(ffn.MoeFfnError) as e:
+        ffn.moe_ffn_plan_get_routing_layout(None)
+    assert e.value.status == ffn.ERR_INVALID_ARG
 
 
 def test_plan_with_the_largest_expert_count_and_top_k(lib):

@@ -34,6 +34,11 @@ SMALL = {
     # the largest expert count and top-k: 512 experts (two per scanning thread), 32 picks a
     # token (128 pairs per ranking workgroup), 20 to 300 tokens: the batch launches
     "bf16_e512_k32": (synth.LayerShape(128, 512, 32, 128, 128, "bf16", "bf16"), 49, (20, 100, 300), 0),
+    # the prefill GEMM's 192- and 256-token passes with its pipelined K loop running (it
+    # needs at least 5 stages of 64: K >= 320 in gate/up (K = hidden 512) and in down
+    # (K = inter 384)): mean buckets of 100 (192-token passes), 200 and 300 (256-token
+    # passes; at 300 most buckets take a second, partial pass)
+    "bf16_prefill_passes": (synth.LayerShape(512, 8, 2, 384, 384, "bf16", "bf16"), 50, (400, 800, 1200), 0),
 }
 
 
@@ -98,6 +103,10 @@ FULL = {
     # name: (shape, seed, tokens, sampled tokens checked against the oracle)
     "decode_bf16_t2048": (synth.DECODE_BF16, 5, 2048, 48),
     "decode_q4_t512": (synth.DECODE_Q4, 6, 512, 32),
+    # the prefill workloads as the benchmark runs them: mean buckets of 128 tokens
+    # (192-token passes) and 512 tokens (256-token passes), K = 2048 and 512
+    "prefill_bf16_t4096": (synth.DECODE_BF16, 9, 4096, 32),
+    "prefill_bf16_t16384": (synth.DECODE_BF16, 10, 16384, 32),
 }
 
 
