@@ -288,6 +288,25 @@ moe_ffn_status moe_ffn_forward(moe_ffn_plan_t plan, const moe_ffn_tensors *tenso
                                int32_t n_tokens, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation): the same
+ * forward, with the workspace taken from a static array the library holds on
+ * each device (MOE_FFN_NOALLOC_WORKSPACE_BYTES per GPU, held until the process
+ * ends) instead of caller memory.  The caller passes inputs and outputs only.
+ * A plan whose workspace_bytes exceed the array is rejected with
+ * MOE_FFN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the decode layer
+ * of hidden 2048, 256 experts, top-8, inter 512 fits up to 128 tokens).  It
+ * allocates nothing: the first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress); the plan's own first-forward set-up is that
+ * of moe_ffn_forward.  Every call on one GPU, from any plan, shares that GPU's
+ * array, which keeps the last call's contents (no call reads them): calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results; serialise them.  Results are bit-identical to moe_ffn_forward's.
+ * Other statuses as moe_ffn_forward. */
+#define MOE_FFN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+moe_ffn_status moe_ffn_forward_noalloc(moe_ffn_plan_t plan, const moe_ffn_tensors *tensors,
+                                       int32_t n_tokens, hipStream_t stream);
+
 /* Releases the plan, its stream and events (waits for the plan's own stream
  * to drain).  NULL is a no-op. */
 void moe_ffn_destroy(moe_ffn_plan_t plan);

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "lib", "libmoe_ffn.so")
 
 ABI_VERSION = 2
+NOALLOC_WORKSPACE_BYTES = 16 << 20  # MOE_FFN_NOALLOC_WORKSPACE_BYTES
 
 # moe_ffn_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL = 0, 1, 2, 3
@@ -101,6 +102,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.moe_ffn_forward.restype = ctypes.c_int32
     lib.moe_ffn_forward.argtypes = [_P, ctypes.POINTER(Tensors), ctypes.c_int32, _P,
                                     ctypes.c_size_t, _P]
+    lib.moe_ffn_forward_noalloc.restype = ctypes.c_int32
+    lib.moe_ffn_forward_noalloc.argtypes = [_P, ctypes.POINTER(Tensors), ctypes.c_int32, _P]
     lib.moe_ffn_destroy.restype = None
     lib.moe_ffn_destroy.argtypes = [_P]
     lib.moe_ffn_profile_enable.restype = ctypes.c_int32
@@ -157,6 +160,11 @@ def moe_ffn_forward(plan: int, tensors: Tensors, n_tokens: int, workspace: int,
                     workspace_bytes: int, stream: int) -> None:
     _check(load().moe_ffn_forward(plan, ctypes.byref(tensors), n_tokens, workspace,
                                   workspace_bytes, stream), "moe_ffn_forward")
+
+
+def moe_ffn_forward_noalloc(plan: int, tensors: Tensors, n_tokens: int, stream: int) -> None:
+    _check(load().moe_ffn_forward_noalloc(plan, ctypes.byref(tensors), n_tokens, stream),
+           "moe_ffn_forward_noalloc")
 
 
 def moe_ffn_destroy(plan: int) -> None:

@@ -223,6 +223,21 @@ def test_routing_layout_lies_in_the_routing_region(lib, T):
     assert e.value.status == ffn.ERR_INVALID_ARG
 
 
+def test_noalloc_refuses_before_any_device_call(lib):
+    # a NULL plan, and a plan whose workspace exceeds the static array, are refused
+    # before the entry point touches the device (this runs without a GPU)
+    t = ffn.Tensors()
+    assert lib.moe_ffn_forward_noalloc(None, ctypes.byref(t), 1, None) == ffn.ERR_INVALID_ARG
+    plan, ws = ffn.moe_ffn_plan(desc(max_tokens=2048))
+    assert ws > ffn.NOALLOC_WORKSPACE_BYTES
+    assert lib.moe_ffn_forward_noalloc(plan, ctypes.byref(t), 1, None) == ffn.ERR_WORKSPACE_TOO_SMALL
+    assert b"static workspace" in lib.moe_ffn_last_error()
+    ffn.moe_ffn_destroy(plan)
+    plan, ws = ffn.moe_ffn_plan(desc(max_tokens=128))  # the decode layer fits up to 128 tokens
+    ffn.moe_ffn_destroy(plan)
+    assert ws <= ffn.NOALLOC_WORKSPACE_BYTES
+
+
 def test_plan_with_the_largest_expert_count_and_top_k(lib):
     # 512 experts x top-32 at 256 tokens: batch routing's ints for 8192 pairs
     E, k, T = 512, 32, 256
