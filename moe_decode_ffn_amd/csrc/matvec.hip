@@ -328,9 +328,11 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     constexpr bool route_here = RH;
     // Loads go out in the order their data is needed (memory returns them in issue
     // order): the batch's logits rows when routing here (at most 5 16-byte chunks per
-    // thread, e.g. 16 tokens of 256 experts), then the tokens resident in the stage (at most kStageBytes:
-    // 8 chunks per thread), then the first job's weights.  The logits reach LDS as soon
-    // as they arrive, the tokens wait in registers through the routing.
+    // thread, e.g. 16 tokens of 256 experts), then the tokens resident in the stage (at most
+    // kStageBytes: 8 chunks per thread), then the first job's weights.  Logits and tokens
+    // reach LDS together before the routing, so that nothing between the bucketing and the
+    // first computation waits for a load (a barrier that also waited for memory would hold
+    // back the first job's weight loads and, behind them, the second job's).
     constexpr int kLgPre = 5, kXPre = 8;
     const int n16lg = route_here ? T * logit_stride(p.E) / 4 : 0;
     uint4 lgpre[kLgPre];
@@ -356,17 +358,82 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
 #pragma unroll
         for (int q = 0; q < kLgPre; ++q)
             if (tid + 256 * q < n16lg) reinterpret_cast<uint4 *>(lgt)[tid + 256 * q] = lgpre[q];
+        if (p.x_resident) {
+#pragma unroll
+            for (int q = 0; q < kXPre; ++q) stage_store(tid + 256 * q, xpre[q], tid + 256 * q < n16);
+        }
         lds_barrier();
         const bool pub = blockIdx.x == 0;
         RouteGlobal g{};
         if (pub) g = RouteGlobal{p.ids, p.wts, p.gate_s, const_cast<int *>(p.records),
                                  const_cast<int *>(p.n_unique), const_cast<int *>(p.pairs), p.pos_expert,
                                  p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
-        rank_tokens(lgt, 0, T, p.E, k, area, L, g, false);
-        nu = bucket_tokens(T, k, p.E, area, L, g);
-        nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
         recs = reinterpret_cast<const int *>(area + L.slots);  // 4-int bucket slots
         prs = reinterpret_cast<const int *>(area + L.pairs);
+        if (T == 1) {
+            // One token: its k picks are k distinct experts, one bucket each in rank order,
+            // so the workgroup's first routed job (bucket `need`) can issue its weight loads
+            // as soon as pick `need` is known; the remaining rounds, the weights and the
+            // tables are done while those loads are in flight (no bucketing step).
+            const int fs = j - p.tiles_shared;
+            const int need = (!loaded && fs >= 0 && fs / p.tiles_routed < k) ? fs / p.tiles_routed : -1;
+            int *lids = reinterpret_cast<int *>(area + L.ids);
+            int *lprs = reinterpret_cast<int *>(area + L.pairs);
+            int *lpose = reinterpret_cast<int *>(area + L.pose);
+            int4 *lslots = reinterpret_cast<int4 *>(area + L.slots);
+            auto one = [&](auto epl) {
+                TokenRank<decltype(epl)::value> st;
+                // wave 0 lanes r0..r1-1 hold picks r0..r1-1: their buckets
+                auto publish = [&](int r0, int r1) {
+                    if (wave == 0 && lane >= r0 && lane < r1) {
+                        const int e = (int)st.my_id;
+                        lslots[lane] = make_int4(e, lane, 1, 0);
+                        lprs[lane] = lane;
+                        lpose[lane] = e;
+                    }
+                };
+                if (wave == 0) {
+                    st.begin(lgt, p.E, lane);
+                    st.rounds(0, need + 1, lane);
+                }
+                publish(0, need + 1);
+                lds_barrier();
+                nu = k;
+                if (need >= 0) {
+                    ja = decode(j);
+                    load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
+                    loaded = true;
+                }
+                if (wave == 0) {
+                    st.rounds(need + 1, k, lane);
+                    publish(need + 1, k);
+                    const RouteOut o{lids, g.wts ? g.wts : reinterpret_cast<float *>(area + L.w),
+                                     g.gate_s ? g.gate_s : reinterpret_cast<float *>(area + L.g),
+                                     g.dbg_ids, g.dbg_w, g.dbg_gate, g.dbg_logits};
+                    st.finish(lgt, p.E, k, lane, o);
+                    if (pub && lane < k) {
+                        // the tables the later launches read: bucket `lane` holds pair `lane`
+                        const int e = (int)st.my_id;
+                        int4 *rec = reinterpret_cast<int4 *>(g.records + lane * kRecInts);
+                        rec[0] = make_int4(e, lane, 1, 0);
+                        rec[1] = make_int4(lane, -1, -1, -1);
+                        rec[2] = make_int4(-1, -1, -1, -1);
+                        rec[3] = make_int4(-1, -1, -1, -1);
+                        g.ids[lane] = e;
+                        g.pairs[lane] = lane;
+                        g.pos_expert[lane] = e;
+                        if (lane == 0) *g.n_unique = k;
+                    }
+                }
+                lds_barrier();
+            };
+            if (p.E <= 256) one(std::integral_constant<int, 4>{});
+            else one(std::integral_constant<int, 8>{});
+        } else {
+            rank_tokens(lgt, 0, T, p.E, k, area, L, g, false);
+            nu = bucket_tokens(T, k, p.E, area, L, g);
+        }
+        nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
     }
     const int J = p.tiles_shared + nu * p.tiles_routed;
     if (j >= J) return;
@@ -374,11 +441,13 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         ja = decode(j);
         load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
     }
-    // tokens staged once (the stage holds the batch) or per pass inside each job
-    if (p.x_resident) {
+    // tokens staged once (the stage holds the batch; with routing here that is done
+    // above) or per pass inside each job; the barrier orders LDS only, so the first job's
+    // weight loads stay in flight across it
+    if (p.x_resident && !route_here) {
 #pragma unroll
         for (int q = 0; q < kXPre; ++q) stage_store(tid + 256 * q, xpre[q], tid + 256 * q < n16);
-        __syncthreads();
+        lds_barrier();
     }
 
     // one job's tokens; RES: the stage holds the whole batch (no memory access or barrier

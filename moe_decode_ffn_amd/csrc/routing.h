@@ -72,66 +72,86 @@ __device__ __forceinline__ void slot_order(uint32_t &ka, uint32_t &ia, uint32_t 
 // Weights: p_e = exp(l_e - max l) / sum_all exp(.) renormalised over the picks
 // is w_j = exp(l_j - m) / sum_picks exp(l_i - m) for any m (the full sum
 // cancels); m = the first pick, the largest logit.
+// The ranking of one token by one wave in phases, so that a caller can act on the
+// first picks before the last are known: begin (keys and the in-lane sort), rounds
+// [r0, r1) (pick r in lane r), finish (weights, gate and outputs).
+template <int EPL>
+struct TokenRank {
+    uint32_t key[EPL], idx[EPL];
+    uint32_t my_id = 0, my_key = 0;
+    float glog = 0.f;
+
+    __device__ __forceinline__ void begin(const float *lg, int E, int lane) {
+        if constexpr (EPL % 4 == 0) {
+            // whole 16-byte groups: a group that starts below E lies inside the padded row
+#pragma unroll
+            for (int v = 0; v < EPL / 4; ++v) {
+                const int e0 = lane * EPL + 4 * v;
+                const float4 f = e0 < E ? *reinterpret_cast<const float4 *>(lg + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) key[4 * v + q] = e0 + q < E ? max(logit_key(fv[q]), 1u) : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                key[i] = e < E ? max(logit_key(lg[e]), 1u) : 0u;
+            }
+        }
+        glog = lg[E];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) idx[i] = (uint32_t)(lane * EPL + i);
+        // in-lane sort: odd-even transposition, EPL rounds
+#pragma unroll
+        for (int r = 0; r < EPL; ++r)
+#pragma unroll
+            for (int i = r & 1; i + 1 < EPL; i += 2) slot_order(key[i], idx[i], key[i + 1], idx[i + 1]);
+    }
+
+    __device__ __forceinline__ void rounds(int r0, int r1, int lane) {
+        for (int r = r0; r < r1; ++r) {
+            const uint32_t M = wave_max_u32(key[0]);
+            const unsigned long long hit = __ballot(key[0] == M);
+            const int wl = (int)__builtin_ctzll(hit);
+            const uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], wl);
+            if (lane == wl) {
+#pragma unroll
+                for (int i = 0; i + 1 < EPL; ++i) { key[i] = key[i + 1]; idx[i] = idx[i + 1]; }
+                key[EPL - 1] = 0u;
+            }
+            if (lane == r) { my_id = win; my_key = M; }
+        }
+    }
+
+    __device__ __forceinline__ void finish(const float *lg, int E, int k, int lane, const RouteOut &o) {
+        const float my_v = key_logit(my_key);
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+        const float myp = lane < k ? expf(my_v - m) : 0.f;
+        const float psum = seg_sum<64>(myp);
+        if (lane < k) {
+            const float w = myp / psum;
+            o.ids[lane] = (int)my_id;
+            o.w[lane] = w;
+            if (o.dbg_ids) o.dbg_ids[lane] = (int)my_id;
+            if (o.dbg_w) o.dbg_w[lane] = w;
+        }
+        if (lane == 0) {
+            const float s = sigmoid_f(glog);
+            o.gate[0] = s;
+            if (o.dbg_gate) o.dbg_gate[0] = s;
+        }
+        if (o.dbg_logits)
+            for (int e = lane; e < E; e += 64) o.dbg_logits[e] = lg[e];
+    }
+};
+
 template <int EPL>
 __device__ void route_token(const float *lg, int E, int k, int lane, const RouteOut &o) {
-    uint32_t key[EPL], idx[EPL];
-    if constexpr (EPL % 4 == 0) {
-        // whole 16-byte groups: a group that starts below E lies inside the padded row
-#pragma unroll
-        for (int v = 0; v < EPL / 4; ++v) {
-            const int e0 = lane * EPL + 4 * v;
-            const float4 f = e0 < E ? *reinterpret_cast<const float4 *>(lg + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) key[4 * v + q] = e0 + q < E ? max(logit_key(fv[q]), 1u) : 0u;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            key[i] = e < E ? max(logit_key(lg[e]), 1u) : 0u;
-        }
-    }
-    const float glog = lg[E];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) idx[i] = (uint32_t)(lane * EPL + i);
-    // in-lane sort: odd-even transposition, EPL rounds
-#pragma unroll
-    for (int r = 0; r < EPL; ++r)
-#pragma unroll
-        for (int i = r & 1; i + 1 < EPL; i += 2) slot_order(key[i], idx[i], key[i + 1], idx[i + 1]);
-
-    uint32_t my_id = 0, my_key = 0;
-    for (int r = 0; r < k; ++r) {
-        const uint32_t M = wave_max_u32(key[0]);
-        const unsigned long long hit = __ballot(key[0] == M);
-        const int wl = (int)__builtin_ctzll(hit);
-        const uint32_t win = (uint32_t)__builtin_amdgcn_readlane((int)idx[0], wl);
-        if (lane == wl) {
-#pragma unroll
-            for (int i = 0; i + 1 < EPL; ++i) { key[i] = key[i + 1]; idx[i] = idx[i + 1]; }
-            key[EPL - 1] = 0u;
-        }
-        if (lane == r) { my_id = win; my_key = M; }
-    }
-    const float my_v = key_logit(my_key);
-    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
-    const float myp = lane < k ? expf(my_v - m) : 0.f;
-    const float psum = seg_sum<64>(myp);
-    if (lane < k) {
-        const float w = myp / psum;
-        o.ids[lane] = (int)my_id;
-        o.w[lane] = w;
-        if (o.dbg_ids) o.dbg_ids[lane] = (int)my_id;
-        if (o.dbg_w) o.dbg_w[lane] = w;
-    }
-    if (lane == 0) {
-        const float s = sigmoid_f(glog);
-        o.gate[0] = s;
-        if (o.dbg_gate) o.dbg_gate[0] = s;
-    }
-    if (o.dbg_logits)
-        for (int e = lane; e < E; e += 64) o.dbg_logits[e] = lg[e];
+    TokenRank<EPL> st;
+    st.begin(lg, E, lane);
+    st.rounds(0, k, lane);
+    st.finish(lg, E, k, lane, o);
 }
 
 __device__ __forceinline__ void route_token_any(const float *lg, int E, int k, int lane, const RouteOut &o) {
