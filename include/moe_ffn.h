@@ -207,10 +207,13 @@ typedef struct moe_ffn_routing_layout {
     size_t records;       /* int32 [U][record_ints]: one job record per used expert:
                              (expert, first bucketed position, pair count, 0, then the
                              first record_pairs pair ids of its bucket, -1 past the count);
-                             experts ascending, except for one token, whose k experts
-                             keep its rank order */
+                             up to 16 tokens in order of first appearance (record u is the
+                             expert of the u-th pair, in pair order, that is the first to
+                             pick its expert; for one token, its rank order), above 16
+                             tokens experts ascending */
     size_t pairs;         /* int32 [T*k]: pair ids in bucketed order; each expert's bucket
-                             is contiguous and holds its pairs in ascending order */
+                             is contiguous and holds its pairs in ascending order; buckets
+                             laid out with experts ascending (one token: rank order) */
     size_t pair_expert;   /* int32 [T*k]: expert of each bucketed position */
     int32_t record_ints;  /* ints per job record */
     int32_t record_pairs; /* pair ids held in a record */

@@ -137,6 +137,11 @@ __device__ __forceinline__ float dot_q4_f32(uint4 w, const float (&a)[32]) {
     return acc;
 }
 
+// Marks a loaded value as used (no instruction): the compiler waits for the load here.
+__device__ __forceinline__ void consume(const uint4 &v) {
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
 // ---- jobs -----------------------------------------------------------------------------------
 struct Job {
     bool valid, routed;
@@ -362,6 +367,14 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
 #pragma unroll
             for (int q = 0; q < kXPre; ++q) stage_store(tid + 256 * q, xpre[q], tid + 256 * q < n16);
         }
+        // every prefetch register counts as consumed here on every path (its stores above are
+        // conditional): otherwise the compiler treats an unused one as still loading and, when
+        // it reuses that register later, waits for every load issued since -- the first job's
+        // weights among them
+#pragma unroll
+        for (int q = 0; q < kLgPre; ++q) consume(lgpre[q]);
+#pragma unroll
+        for (int q = 0; q < kXPre; ++q) consume(xpre[q]);
         lds_barrier();
         const bool pub = blockIdx.x == 0;
         RouteGlobal g{};
@@ -370,68 +383,89 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                                  p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
         recs = reinterpret_cast<const int *>(area + L.slots);  // 4-int bucket slots
         prs = reinterpret_cast<const int *>(area + L.pairs);
-        if (T == 1) {
-            // One token: its k picks are k distinct experts, one bucket each in rank order,
-            // so the workgroup's first routed job (bucket `need`) can issue its weight loads
-            // as soon as pick `need` is known; the remaining rounds, the weights and the
-            // tables are done while those loads are in flight (no bucketing step).
-            const int fs = j - p.tiles_shared;
-            const int need = (!loaded && fs >= 0 && fs / p.tiles_routed < k) ? fs / p.tiles_routed : -1;
-            int *lids = reinterpret_cast<int *>(area + L.ids);
-            int *lprs = reinterpret_cast<int *>(area + L.pairs);
-            int *lpose = reinterpret_cast<int *>(area + L.pose);
-            int4 *lslots = reinterpret_cast<int4 *>(area + L.slots);
-            auto one = [&](auto epl) {
-                TokenRank<decltype(epl)::value> st;
-                // wave 0 lanes r0..r1-1 hold picks r0..r1-1: their buckets
-                auto publish = [&](int r0, int r1) {
-                    if (wave == 0 && lane >= r0 && lane < r1) {
-                        const int e = (int)st.my_id;
-                        lslots[lane] = make_int4(e, lane, 1, 0);
-                        lprs[lane] = lane;
-                        lpose[lane] = e;
-                    }
-                };
-                if (wave == 0) {
-                    st.begin(lgt, p.E, lane);
-                    st.rounds(0, need + 1, lane);
+        // Buckets are numbered in order of first appearance, so buckets 0..k-1 are token
+        // 0's picks in rank order.  The workgroup's first routed job (bucket `need`, one of
+        // those) issues its weight loads as soon as wave 0 has ranked that pick; the rest of
+        // the routing (the other picks and tokens, weights, bucketing and tables) runs while
+        // the loads are in flight, and the job learns its tokens from the finished buckets.
+        // One token needs no bucketing: its k picks are k buckets of one pair each.
+        const int fs = j - p.tiles_shared;
+        const int need = (!loaded && fs >= 0 && fs / p.tiles_routed < k) ? fs / p.tiles_routed : -1;
+        int *lids = reinterpret_cast<int *>(area + L.ids);
+        int *lprs = reinterpret_cast<int *>(area + L.pairs);
+        int *lpose = reinterpret_cast<int *>(area + L.pose);
+        int4 *lslots = reinterpret_cast<int4 *>(area + L.slots);
+        float *lw = reinterpret_cast<float *>(area + L.w);
+        float *lg1 = reinterpret_cast<float *>(area + L.g);
+        int early_e = -1;
+        auto route = [&](auto epl) {
+            TokenRank<decltype(epl)::value> st;
+            // wave 0 lanes r0..r1-1 hold token 0's picks r0..r1-1: their buckets (final for
+            // one token; for more tokens only the expert is read before the bucketing
+            // rewrites the slots)
+            auto publish = [&](int r0, int r1) {
+                if (wave == 0 && lane >= r0 && lane < r1) {
+                    const int e = (int)st.my_id;
+                    lslots[lane] = make_int4(e, lane, 1, 0);
+                    lprs[lane] = lane;
+                    lpose[lane] = e;
                 }
-                publish(0, need + 1);
-                lds_barrier();
-                nu = k;
-                if (need >= 0) {
-                    ja = decode(j);
-                    load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
-                    loaded = true;
-                }
-                if (wave == 0) {
-                    st.rounds(need + 1, k, lane);
-                    publish(need + 1, k);
-                    const RouteOut o{lids, g.wts ? g.wts : reinterpret_cast<float *>(area + L.w),
-                                     g.gate_s ? g.gate_s : reinterpret_cast<float *>(area + L.g),
-                                     g.dbg_ids, g.dbg_w, g.dbg_gate, g.dbg_logits};
-                    st.finish(lgt, p.E, k, lane, o);
-                    if (pub && lane < k) {
-                        // the tables the later launches read: bucket `lane` holds pair `lane`
-                        const int e = (int)st.my_id;
-                        int4 *rec = reinterpret_cast<int4 *>(g.records + lane * kRecInts);
-                        rec[0] = make_int4(e, lane, 1, 0);
-                        rec[1] = make_int4(lane, -1, -1, -1);
-                        rec[2] = make_int4(-1, -1, -1, -1);
-                        rec[3] = make_int4(-1, -1, -1, -1);
-                        g.ids[lane] = e;
-                        g.pairs[lane] = lane;
-                        g.pos_expert[lane] = e;
-                        if (lane == 0) *g.n_unique = k;
-                    }
-                }
-                lds_barrier();
             };
-            if (p.E <= 256) one(std::integral_constant<int, 4>{});
-            else one(std::integral_constant<int, 8>{});
+            if (wave == 0) {
+                st.begin(lgt, p.E, lane);
+                st.rounds(0, need + 1, lane);
+            }
+            publish(0, need + 1);
+            lds_barrier();
+            nu = k;
+            if (need >= 0) {
+                ja = decode(j);
+                early_e = lslots[need].x;
+                load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
+                loaded = true;
+            }
+            if (wave == 0) {
+                st.rounds(need + 1, k, lane);
+                publish(need + 1, k);
+                // outputs to LDS only (a store that may go to LDS or memory is a flat store,
+                // and waiting for one would wait for the weight loads in flight)
+                const RouteOut o{lids, lw, lg1, g.dbg_ids, g.dbg_w, g.dbg_gate, g.dbg_logits};
+                st.finish(lgt, p.E, k, lane, o);
+                if (T == 1 && pub && lane < k) {
+                    // the tables the later launches read: bucket `lane` holds pair `lane`
+                    const int e = (int)st.my_id;
+                    int4 *rec = reinterpret_cast<int4 *>(g.records + lane * kRecInts);
+                    rec[0] = make_int4(e, lane, 1, 0);
+                    rec[1] = make_int4(lane, -1, -1, -1);
+                    rec[2] = make_int4(-1, -1, -1, -1);
+                    rec[3] = make_int4(-1, -1, -1, -1);
+                    g.ids[lane] = e;
+                    g.wts[lane] = lw[lane];  // this lane's own store above
+                    g.pairs[lane] = lane;
+                    g.pos_expert[lane] = e;
+                    if (lane == 0) {
+                        *g.n_unique = k;
+                        g.gate_s[0] = lg1[0];
+                    }
+                }
+            }
+        };
+        if (p.E <= 256) route(std::integral_constant<int, 4>{});
+        else route(std::integral_constant<int, 8>{});
+        if (T == 1) {
+            lds_barrier();
         } else {
-            rank_tokens(lgt, 0, T, p.E, k, area, L, g, false);
+            // the other tokens (wave w takes tokens w, w + 4, ...; token 0 is done), then the
+            // bucketing, whose first barrier orders every wave's picks
+            rank_tokens(lgt, 1, T, p.E, k, area, L, g);
             nu = bucket_tokens(T, k, p.E, area, L, g);
+            if (need >= 0) {
+                // the job's tokens: its bucket as finished (the same expert)
+                const int4 sv = lslots[need];
+                ja.ntok = sv.z;
+                ja.valid = ja.valid && need < nu && sv.x == early_e && sv.y >= 0 && sv.z > 0 &&
+                           sv.y + sv.z <= T * k;
+            }
         }
         nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
     }

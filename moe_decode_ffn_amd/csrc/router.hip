@@ -200,7 +200,7 @@ __global__ __launch_bounds__(1024) void k_route(RouterParams p) {
     const RouteLds L = route_lds_layout(p.T, p.k, p.E, false);
     const RouteGlobal g{p.ids, p.wts, p.gate_s, p.records, p.n_unique, p.pairs, p.pos_expert,
                         p.dbg_ids, p.dbg_w, p.dbg_logits, p.dbg_gate};
-    rank_tokens(p.logits, 0, p.T, p.E, p.k, lds, L, g, false);
+    rank_tokens(p.logits, 0, p.T, p.E, p.k, lds, L, g);
     bucket_tokens(p.T, p.k, p.E, lds, L, g);
 }
 

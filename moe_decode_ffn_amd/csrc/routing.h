@@ -162,9 +162,11 @@ __device__ __forceinline__ void route_token_any(const float *lg, int E, int k, i
     else route_token<8>(lg, E, k, lane, o);
 }
 
-// LDS ints the bucketing needs for E experts and T tokens.
-__host__ __device__ inline int bucket_scratch_ints(int E, int T) {
-    return E * ((T + 31) / 32) + 2 * E + 2 * 16 + 16;
+// LDS ints the bucketing needs for E experts, T tokens and k picks a token: token
+// bitmaps [E][ceil(T/32)], counts [E], positions [E], wave totals [32], first pairs [E],
+// first-appearance bits [ceil(T*k/32)].
+__host__ __device__ inline int bucket_scratch_ints(int E, int T, int k) {
+    return E * ((T + 31) / 32) + 3 * E + 2 * 16 + (T * k + 31) / 32 + 16;
 }
 
 // The value of lane (lane ^ J) for J a power of two below 64, in vector registers
@@ -204,8 +206,10 @@ __device__ __forceinline__ uint32_t bitonic_stage(uint32_t key, int lane) {
 // Bucketing of up to 64 pairs by one wave (the same tables as bucket_pairs): lane q
 // holds pair q as the key expert * 64 + q; a bitonic sort over the wave puts the keys
 // in (expert, pair) order, so lane q then holds bucket position q; a bucket starts
-// where the expert changes from the lane below, and its slot is the number of bucket
-// starts below it.  All 64 lanes of the wave must be active.
+// where the expert changes from the lane below.  Buckets are numbered in order of first
+// appearance: a bucket's first pair is the first pair that picked its expert, and its
+// slot is the number of buckets whose first pair comes earlier.  All 64 lanes of the
+// wave must be active.
 __device__ inline void bucket_pairs_wave(const int *ids, int NP, int E, int4 *slots, int *pairs,
                                          int *pos_expert, int *n_unique) {
     const int lane = threadIdx.x & 63;
@@ -238,37 +242,49 @@ __device__ inline void bucket_pairs_wave(const int *ids, int NP, int E, int4 *sl
     const bool first = ok && (lane == 0 || below != e);
     const unsigned long long fm = __ballot(first);
     const int nvalid = __popcll(__ballot(ok));  // valid pairs: the last bucket ends there
+    const int nb = __popcll(fm);
+    const int q = (int)(key & 63u);
     if (ok) {
-        pairs[lane] = (int)(key & 63u);
+        pairs[lane] = q;
         pos_expert[lane] = e;
     }
+    // each sorted lane tells the lane of its pair whether that pair opens a bucket (a
+    // permutation of the wave: the lanes past the valid pairs keep their own), so that
+    // bit q of `om` says whether pair q is the first of its expert
+    const int opens = __builtin_amdgcn_ds_permute((ok ? q : lane) << 2, first ? 1 : 0);
+    const unsigned long long om = __ballot(opens != 0 && lane < NP);
     if (first) {
-        const int u = __popcll(fm & ((1ull << lane) - 1ull));
+        const int u = __popcll(om & ((1ull << q) - 1ull));
         const unsigned long long after = lane == 63 ? 0ull : fm & ~((2ull << lane) - 1ull);
         const int end = after ? (int)__builtin_ctzll(after) : nvalid;
-        slots[u] = make_int4(e, lane, end - lane, 0);
+        if (u < nb) slots[u] = make_int4(e, lane, end - lane, 0);
     }
-    if (lane == 0) *n_unique = __popcll(fm);
+    if (lane == 0) *n_unique = nb;
 }
 
 // Bucketing of all T*k pairs by one workgroup (any multiple of 64 threads up
 // to 1024).  ids[], the scratch and the outputs are in LDS (the barriers
 // inside order LDS accesses only).  Outputs:
-// slots[u] = (expert, first position, count, 0) for used experts in ascending
-// order, pairs[pos] = t*k + j, pos_expert[pos], *n_unique.  Positions are
-// expert-major, tokens ascending within an expert; a token's rank in its
-// expert's bucket is the number of earlier tokens in the expert's token bitmap
-// (a token picks an expert at most once).  Integer only: the result is unique.
+// slots[u] = (expert, first position, count, 0) for used experts in order of first
+// appearance (slot u is the expert of the u-th pair, in pair order, that is the first
+// to pick its expert), pairs[pos] = t*k + j, pos_expert[pos], *n_unique.  Positions
+// are expert-major (experts ascending), tokens ascending within an expert; a token's
+// rank in its expert's bucket is the number of earlier tokens in the expert's token
+// bitmap (a token picks an expert at most once).  Integer only: the result is unique.
 __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scratch, int4 *slots,
                              int *pairs, int *pos_expert, int *n_unique) {
     const int nth = blockDim.x, nw = nth >> 6;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int NP = T * k, W = (T + 31) / 32;
+    const int NW = (NP + 31) / 32;
     uint32_t *mask = scratch;                     // [E][W] token bitmaps
     int *cnt = (int *)(mask + (size_t)E * W);     // [E]
     int *off = cnt + E;                           // [E] first position of expert e
     int *wtot = off + E;                          // [2 * 16] wave totals
+    int *fq = wtot + 32;                          // [E] first pair of expert e
+    uint32_t *fbits = (uint32_t *)(fq + E);       // [NW] bit q: pair q is the first of its expert
     for (int i = tid; i < E * W; i += nth) mask[i] = 0u;
+    for (int i = tid; i < NW; i += nth) fbits[i] = 0u;
     lds_barrier();
     for (int q = tid; q < NP; q += nth) {
         const int t = q / k, e = ids[q];
@@ -276,9 +292,18 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
     }
     lds_barrier();
     for (int e = tid; e < E; e += nth) {
-        int c = 0;
-        for (int w = 0; w < W; ++w) c += __popc(mask[e * W + w]);
+        int c = 0, t0 = -1;
+        for (int w = 0; w < W; ++w) {
+            const uint32_t m = mask[e * W + w];
+            c += __popc(m);
+            if (t0 < 0 && m) t0 = 32 * w + __builtin_ctz(m);
+        }
         cnt[e] = c;
+        int q0 = -1;  // the first token that picked e, at the slot where it did
+        for (int jj = 0; t0 >= 0 && jj < k && q0 < 0; ++jj)
+            if (ids[t0 * k + jj] == e) q0 = t0 * k + jj;
+        fq[e] = q0;
+        if (q0 >= 0) atomicOr(&fbits[q0 >> 5], 1u << (q0 & 31));
     }
     lds_barrier();
     // exclusive scans of cnt[] and (cnt[] > 0); thread owns EPT consecutive experts
@@ -295,15 +320,20 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
     }
     if (lane == 63) { wtot[wave] = ia; wtot[16 + wave] = ib; }
     lds_barrier();
-    int ba = ia - a, bb = ib - b;
-    for (int w = 0; w < wave; ++w) { ba += wtot[w]; bb += wtot[16 + w]; }
+    int ba = ia - a;
+    for (int w = 0; w < wave; ++w) ba += wtot[w];
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
         if (e < E) {
             off[e] = ba;
-            if (cnt[e] > 0) slots[bb] = make_int4(e, ba, cnt[e], 0);
+            const int q0 = fq[e];
+            if (cnt[e] > 0 && q0 >= 0 && q0 < NP) {
+                // slot = first pairs of other experts that come before this one's
+                int u = __popc(fbits[q0 >> 5] & ((1u << (q0 & 31)) - 1u));
+                for (int w = 0; w < (q0 >> 5); ++w) u += __popc(fbits[w]);
+                slots[u] = make_int4(e, ba, cnt[e], 0);
+            }
             ba += cnt[e];
-            bb += cnt[e] > 0;
         }
     }
     if (tid == nth - 1) {
@@ -350,12 +380,10 @@ __host__ __device__ inline RouteLds route_lds_layout(int T, int k, int E, bool l
     L.nu = o;      o += 16;
     o = (o + 15) & ~(size_t)15;
     L.slots = o;   o += ns * 16;
-    L.scratch = o; o += (size_t)bucket_scratch_ints(E, T) * 4;
+    L.scratch = o; o += (size_t)bucket_scratch_ints(E, T, k) * 4;
     o = (o + 15) & ~(size_t)15;
-    if (local) {
-        L.w = o;       o += np * 4;
-        L.g = o;       o += (size_t)T * 4;
-    }
+    L.w = o;       o += np * 4;
+    L.g = o;       o += (size_t)T * 4;
     o = (o + 15) & ~(size_t)15;
     L.lgt = o;     o += local ? (size_t)T * logit_stride(E) * 4 : 0;
     L.bytes = (o + 15) & ~(size_t)15;
@@ -379,14 +407,17 @@ struct RouteGlobal {
 // gates go to g when g.wts is set, else to LDS.  logits: row 0 of the [T][stride]
 // table, in memory or in LDS.  No barrier inside.
 __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int E, int k, uint8_t *area,
-                                   const RouteLds &L, const RouteGlobal &g, bool ids_to_global) {
+                                   const RouteLds &L, const RouteGlobal &g) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     int *ids = reinterpret_cast<int *>(area + L.ids);
     float *lw = reinterpret_cast<float *>(area + L.w);
     float *lg = reinterpret_cast<float *>(area + L.g);
-    for (int t = t_lo + wave; t < t_hi; t += nw) {
-        RouteOut o{(ids_to_global ? g.ids : ids) + t * k, (g.wts ? g.wts : lw) + t * k,
-                   (g.gate_s ? g.gate_s : lg) + t,
+    for (int t = wave; t < t_hi; t += nw) {  // token t on wave t % nw, from t_lo on
+        if (t < t_lo) continue;
+        // every output goes to LDS (one known address space: a store through a pointer that
+        // may be LDS or memory is a flat store, and waiting for one waits for every load in
+        // flight); the publishing workgroup copies the tables to memory after the bucketing
+        RouteOut o{ids + t * k, lw + t * k, lg + t,
                    g.dbg_ids ? g.dbg_ids + t * k : nullptr, g.dbg_w ? g.dbg_w + t * k : nullptr,
                    g.dbg_gate ? g.dbg_gate + t : nullptr,
                    g.dbg_logits ? g.dbg_logits + (size_t)t * E : nullptr};
@@ -437,12 +468,17 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
         else v = (f - 4 < sv.z) ? pairs[sv.y + f - 4] : -1;
         g.records[i] = v;
     }
-    if (g.ids)
+    if (g.ids) {
+        const float *lw = reinterpret_cast<const float *>(area + L.w);
+        const float *lg = reinterpret_cast<const float *>(area + L.g);
         for (int i = tid; i < NP; i += blockDim.x) {
             g.ids[i] = ids[i];
+            g.wts[i] = lw[i];
             g.pairs[i] = pairs[i];
             g.pos_expert[i] = pose[i];
         }
+        for (int i = tid; i < T; i += blockDim.x) g.gate_s[i] = lg[i];
+    }
     if (g.n_unique && tid == 0) *g.n_unique = nu;
     lds_barrier();
     return nu;

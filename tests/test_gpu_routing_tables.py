@@ -1,7 +1,9 @@
 """GPU: the routing step's integer tables, read from the workspace after a forward,
 equal their definition exactly (tests/routing_tables.py): every (token, slot) pair
 bucketed once under its expert, buckets contiguous with their pairs ascending, the
-used experts the distinct ids, the job records those of the buckets.
+used experts the distinct ids, the job records those of the buckets -- numbered in
+order of first appearance when one workgroup routes the batch, ascending from the
+batch launches.
 
 Every routing placement is covered: the gate/up workgroups route the batch themselves
 (up to 16 tokens: one token, the one-wave sort up to 64 pairs, the workgroup bitmap
@@ -31,7 +33,7 @@ def _tables(mf, ws, T):
     return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in tab.items()}
 
 
-def _check_call(orc, mf, layer_cpu, dl, x, n_check, modes=("fused",)):
+def _check_call(orc, mf, layer_cpu, dl, x, n_check, modes=("fused",), batch_launches=None):
     """Runs the forward in each mode, checks the tables of each and their agreement,
     and the outputs of up to n_check tokens against the oracle."""
     dev = device()
@@ -46,14 +48,22 @@ def _check_call(orc, mf, layer_cpu, dl, x, n_check, modes=("fused",)):
         ids = got["ids"].numpy()
         assert np.array_equal(tab["ids"].reshape(T, -1), ids), "workspace ids vs debug ids"
         assert np.array_equal(tab["weights"].reshape(T, -1), got["weights"].numpy())
-        check_tables(tab, ids)
-        tabs[m] = (tab, got)
+        tabs[m] = (tab, got, check_tables(tab, ids))
     first = tabs[modes[0]][0]
     for m in modes[1:]:
         t = tabs[m][0]
         for key in ("n_used", "records", "pairs", "pair_expert", "ids"):
             assert np.array_equal(np.asarray(first[key]), np.asarray(t[key])), f"{key}: {modes[0]} vs {m}"
     got = tabs[modes[0]][1]
+    orders = tabs[modes[0]][2]
+    if batch_launches is not None:
+        # records: ascending from the batch launches, first appearance from one workgroup
+        # (the two coincide when the first appearances happen to be ascending)
+        from tests.routing_tables import expert_order
+        ids = got["ids"].numpy()
+        same = expert_order(ids, "ascending") == expert_order(ids, "first")
+        want = "ascending" if batch_launches else "first"
+        assert orders[0] == want or same, f"record order {orders[0]}, expected {want}"
     idx = np.arange(T) if n_check >= T else np.sort(np.random.default_rng(T).choice(T, n_check, replace=False))
     sel = torch.from_numpy(idx)
     sub = {k: v[sel] for k, v in got.items()}
@@ -80,7 +90,7 @@ def test_decode_layer_tables(orc, decode_layer, T):
     x = synth.make_tokens(shape, T, 31, stream=T)
     plans = {m: ffn.MoeFfn.for_shape(shape, max_tokens=T, flags=f) for m, f in MODES.items()}
     print(f"[tables] decode bf16 T={T}", flush=True)
-    tab = _check_call(orc, plans, lc, dl, x, n_check=16, modes=tuple(MODES))
+    tab = _check_call(orc, plans, lc, dl, x, n_check=16, modes=tuple(MODES), batch_launches=T > 16)
     print(f"  used experts {tab['n_used']}", flush=True)
     for p in plans.values():
         p.close()

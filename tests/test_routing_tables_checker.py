@@ -20,26 +20,42 @@ def _ids(T, k, E, seed):
     return np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
 
 
-def _tables(ids, rank_order=False):
-    t = expected_tables(ids, RP, rank_order=rank_order)
+def _tables(ids, record_order="ascending", layout_order="ascending"):
+    t = expected_tables(ids, RP, record_order, layout_order)
     t["record_pairs"] = RP
     return t
 
 
+ORDER_PAIRS = [("ascending", "ascending"), ("first", "ascending"), ("first", "first")]
+
+
+@pytest.mark.parametrize("orders", ORDER_PAIRS)
 @pytest.mark.parametrize("T,k,E", [(1, 8, 256), (2, 8, 256), (8, 8, 256), (17, 8, 64), (40, 2, 4), (6, 16, 24)])
-def test_correct_tables_pass(T, k, E):
+def test_correct_tables_pass(T, k, E, orders):
     ids = _ids(T, k, E, T * 1000 + k)
-    check_tables(_tables(ids), ids)
+    assert check_tables(_tables(ids, *orders), ids) in [orders, ("ascending", "ascending"),
+                                                         ("first", "first"), ("first", "ascending")]
 
 
 def test_single_token_in_rank_order_passes():
+    # one token: first appearance is its rank order
     ids = np.array([[7, 3, 200, 1, 9, 100, 50, 2]])
-    check_tables(_tables(ids, rank_order=True), ids)
-    check_tables(_tables(ids), ids)
+    assert check_tables(_tables(ids, "first", "first"), ids) == ("first", "first")
+    assert check_tables(_tables(ids), ids) == ("ascending", "ascending")
 
 
-def _mutants(ids):
-    base = _tables(ids)
+def test_first_appearance_order_by_hand():
+    # pairs 0..5 pick experts 5 3 | 3 9 | 1 5: first appearances 5, 3, 9, 1
+    ids = np.array([[5, 3], [3, 9], [1, 5]])
+    t = _tables(ids, "first", "ascending")
+    assert t["records"][:, 0].tolist() == [5, 3, 9, 1]
+    assert t["records"][:, 1].tolist() == [3, 1, 5, 0]  # positions with experts ascending: 1 3 3 5 5 9
+    assert t["pairs"].tolist() == [4, 1, 2, 0, 5, 3]
+    check_tables(t, ids)
+
+
+def _mutants(ids, orders=("ascending", "ascending")):
+    base = _tables(ids, *orders)
 
     def m(fn):
         t = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in base.items()}
@@ -85,9 +101,10 @@ def _mutants(ids):
                                          no_terminator, pair_expert, n_used, order_of_used)}
 
 
+@pytest.mark.parametrize("orders", ORDER_PAIRS)
 @pytest.mark.parametrize("name", ["dup_pair", "swap_in_bucket", "dup_expert", "count", "start", "inline_pair",
                                   "no_terminator", "pair_expert", "n_used", "order_of_used"])
-def test_planted_mistakes_fail(name):
+def test_planted_mistakes_fail(name, orders):
     ids = _ids(8, 8, 48, 5)  # 64 pairs over at most 48 experts: shared buckets
     with pytest.raises(AssertionError):
-        check_tables(_mutants(ids)[name], ids)
+        check_tables(_mutants(ids, orders)[name], ids)
