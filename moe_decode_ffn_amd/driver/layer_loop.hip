@@ -2,11 +2,13 @@
 // Python, no torch): a plain C-ABI usage example and a small driver for
 // profiler runs (kernel traces, hardware counters).
 //
-//   layer_loop <workload> [mode] [steps] [warmup]
-//     workload: decode_bf16_t1 | decode_bf16_t8 | decode_q4_t1_t4 | decode_bf16_t128 |
-//               prefill_bf16_t4096 | prefill_bf16_t16384 | decode_bf16_t1_tp8 |
-//               decode_bf16_t8_tp8 | tiny_fp32
+//   layer_loop <workload> [mode] [steps] [warmup] [launch]
+//     workload: decode_bf16_t1 | decode_bf16_t8 | decode_q4_t1_t4 | decode_q4_t1 |
+//               decode_bf16_t128 | prefill_bf16_t4096 | prefill_bf16_t16384 |
+//               decode_bf16_t1_tp8 | decode_bf16_t8_tp8 | tiny_fp32
 //     mode:     auto | aux | seq | fused          (default auto)
+//     launch:   eager | graph                     (default eager; graph: one HIP graph
+//               captures a rotation window of forwards and is replayed)
 //
 // Weights and tokens are hash-filled on the device (a fixed seed per layer
 // copy); the layers rotate over enough copies that consecutive uses of one
@@ -83,6 +85,7 @@ const Workload kWorkloads[] = {
     {"decode_bf16_t1", 2048, 256, 8, 512, 512, 1, MOE_FFN_BF16, MOE_FFN_BF16},
     {"decode_bf16_t8", 2048, 256, 8, 512, 512, 8, MOE_FFN_BF16, MOE_FFN_BF16},
     {"decode_q4_t1_t4", 2048, 256, 8, 512, 512, 4, MOE_FFN_BF16, MOE_FFN_Q4_B32},
+    {"decode_q4_t1", 2048, 256, 8, 512, 512, 1, MOE_FFN_BF16, MOE_FFN_Q4_B32},
     {"decode_bf16_t128", 2048, 256, 8, 512, 512, 128, MOE_FFN_BF16, MOE_FFN_BF16},
     {"prefill_bf16_t4096", 2048, 256, 8, 512, 512, 4096, MOE_FFN_BF16, MOE_FFN_BF16},
     {"prefill_bf16_t16384", 2048, 256, 8, 512, 512, 16384, MOE_FFN_BF16, MOE_FFN_BF16},
@@ -144,6 +147,11 @@ int main(int argc, char **argv) {
     }
     const int steps = argc > 3 ? std::atoi(argv[3]) : 2000;
     const int warmup = argc > 4 ? std::atoi(argv[4]) : 200;
+    const std::string launch = argc > 5 ? argv[5] : "eager";
+    if (launch != "eager" && launch != "graph") {
+        std::fprintf(stderr, "unknown launch %s\n", launch.c_str());
+        return 2;
+    }
     const int H = wl->H, E = wl->E, k = wl->k, I = wl->I, Is = wl->Is, T = wl->T;
     const int wd = wl->w_dtype;
 
@@ -213,14 +221,36 @@ int main(int argc, char **argv) {
             }
         }
     };
-    run(warmup, 0);
+    // graph mode: the first forward (the plan's set-up) runs eagerly, then one graph holds a
+    // window of forwards over every layer copy and is replayed
+    hipGraphExec_t exec = nullptr;
+    hipGraph_t graph = nullptr;
+    if (launch == "graph") {
+        run(1, 0);
+        CHECK(hipStreamSynchronize(stream));
+        CHECK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+        run(copies, 0);
+        CHECK(hipStreamEndCapture(stream, &graph));
+        CHECK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+    }
+    auto go = [&](int n, int from) {
+        if (launch == "eager") {
+            run(n, from);
+            return;
+        }
+        for (int i = 0; i < (n + copies - 1) / copies; ++i) CHECK(hipGraphLaunch(exec, stream));
+    };
+    const int done = launch == "graph" ? (steps + copies - 1) / copies * copies : steps;
+    go(warmup, 0);
     CHECK(hipStreamSynchronize(stream));
     const auto t0 = std::chrono::steady_clock::now();
-    run(steps, warmup);
+    go(steps, warmup);
     CHECK(hipStreamSynchronize(stream));
     const double us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
-    std::printf("layer_loop %s H=%d E=%d k=%d I=%d Is=%d T=%d mode=%s copies=%d steps=%d: %.3f us/forward\n",
-                wl->name, H, E, k, I, Is, T, mode.c_str(), copies, steps, us / steps);
+    std::printf("layer_loop %s H=%d E=%d k=%d I=%d Is=%d T=%d mode=%s launch=%s copies=%d steps=%d: %.3f us/forward\n",
+                wl->name, H, E, k, I, Is, T, mode.c_str(), launch.c_str(), copies, done, us / done);
+    if (exec) CHECK(hipGraphExecDestroy(exec));
+    if (graph) CHECK(hipGraphDestroy(graph));
     moe_ffn_destroy(plan);
     CHECK(hipStreamDestroy(stream));
     return 0;
