@@ -8,6 +8,11 @@ here launches a kernel of the layer):
         under `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`: what the
         counters report for known bytes gives the scale factors.
 
+    python -m moe_decode_ffn_amd.traffic counters --dir DIR [--dir DIR ...] --kernel REGEX \\
+        --workload NAME --out FILE [--command CMD ...]
+        Per-dispatch means of the shader counters found under the directories (SQ_*),
+        with instructions per wave and the share of wave cycles issuing or waiting.
+
     python -m moe_decode_ffn_amd.traffic summarize --fetch DIR --write DIR \\
         --cal-fetch DIR --cal-write DIR --cal-mib N --kernel REGEX \\
         --workload NAME --shared-mode MODE --kernel-id ID --out profiles/traffic_<workload>.md
@@ -150,6 +155,43 @@ def cmd_summarize(args) -> int:
     return 0
 
 
+def cmd_counters(args) -> int:
+    """Per-dispatch means of the counters found under each --dir for one kernel, and the
+    ratios that say what bounds it: VALU instructions and cycles per wave, the share of a
+    wave's cycles spent issuing VALU work or waiting."""
+    vals: dict[str, float] = {}
+    n = 0
+    for d in args.dir:
+        for cname, v in per_dispatch(read_counters(d), args.kernel).items():
+            vals[cname] = statistics.mean(v)
+            n = max(n, len(v))
+    lines = [f"# Shader counters: `{args.kernel}`, workload {args.workload}", "",
+             "Means per dispatch of the kernel (rocprofv3 --pmc, at most 8 SQ counters a run).", "",
+             "Commands (from /tmp, one MI355X):", "", "```"] + (args.command or []) + ["```", "",
+             "| counter | mean per dispatch |", "|---|---|"]
+    for cname, v in sorted(vals.items()):
+        lines.append(f"| {cname} | {v:.6g} |")
+    w, wc = vals.get("SQ_WAVES"), vals.get("SQ_WAVE_CYCLES")
+    ratios = []
+    if w:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_INSTS_SMEM"):
+            if c in vals:
+                ratios.append((f"{c} per wave", vals[c] / w))
+        ratios.append(("SQ_WAVE_CYCLES per wave", (wc or 0) / w))
+    if wc:
+        for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS",
+                  "SQ_ACTIVE_INST_SCA", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"):
+            if c in vals:
+                ratios.append((f"{c} / SQ_WAVE_CYCLES", vals[c] / wc))
+    if ratios:
+        lines += ["", "| ratio | value |", "|---|---|"] + [f"| {k} | {v:.4g} |" for k, v in ratios]
+    lines += ["", f"Dispatches: {n}; kernel source hash `{kernel_source_hash()}`.", ""]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def read_summary(path: str) -> dict | None:
     """The fenced `traffic` block of a summary written by summarize, or None."""
     if not os.path.exists(path):
@@ -181,8 +223,14 @@ def main(argv=None) -> int:
                    help="the profiling id of the kernel (moe_ffn_kernel_id name, e.g. gate_up, gg_gate_up)")
     s.add_argument("--extra", action="append")
     s.add_argument("--command", action="append", help="a command line to record in the summary")
+    k = sub.add_parser("counters")
+    k.add_argument("--dir", action="append", required=True)
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--workload", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--command", action="append")
     args = ap.parse_args(argv)
-    return cmd_copy(args) if args.cmd == "copy" else cmd_summarize(args)
+    return {"copy": cmd_copy, "summarize": cmd_summarize, "counters": cmd_counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
