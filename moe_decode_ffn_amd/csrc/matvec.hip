@@ -44,12 +44,12 @@ static int rpw_d_of(int wk) {
                                                              : WTraits<W_Q4>::rpw_d;
 }
 
-// A bf16 batch of up to 3 tokens routed inside the gate/up workgroups reads one row per
-// wave per job instead of two: twice the jobs over more resident workgroups, so the last
-// round of jobs is a smaller part of the launch (from 4 tokens on, the two-row jobs, which
-// read each staged token once for two rows, are faster).
+// A bf16 single token routed inside the gate/up workgroups reads one row per wave per job
+// instead of two: twice the jobs over more resident workgroups, so the last round of jobs
+// is a smaller part of the launch (from 2 tokens on, the two-row jobs, which read each
+// staged token once for two rows, are as fast or faster).
 bool gate_up_one_row(int wkind, const RowMap &m, int T, bool route_here) {
-    return wkind == W_BF16 && m.lpr == 64 && T <= 3 && route_here;
+    return wkind == W_BF16 && m.lpr == 64 && T == 1 && route_here;
 }
 int gate_up_rows_per_wg(int wkind, const RowMap &m, int T, bool route_here) {
     return kWaves * (gate_up_one_row(wkind, m, T, route_here) ? 1 : rpw_gu_of(wkind)) * (64 / m.lpr);
@@ -869,6 +869,41 @@ __global__ __launch_bounds__(256) void k_join(JoinParams p) {
     p.out[(size_t)t * p.H + r] = o;
 }
 
+// The same join four columns a thread (hidden sizes that are a multiple of 4): 16-byte
+// loads and stores, one workgroup per 1024 columns of a token; each column's arithmetic
+// is k_join's, in the same order.
+__global__ __launch_bounds__(256) void k_join4(JoinParams p) {
+    const int t = blockIdx.y;
+    const int r = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (r >= p.H) return;
+    const int k = p.k;
+    const float *wt = p.wts + (size_t)t * k;
+    const float *yr = p.y + (size_t)t * k * p.H + r;
+    float4 yv[kMaxTopK];
+    float wv[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        yv[j] = j < k ? *reinterpret_cast<const float4 *>(yr + (size_t)j * p.H) : make_float4(0.f, 0.f, 0.f, 0.f);
+        wv[j] = j < k ? wt[j] : 0.f;
+    }
+    const float4 S = *reinterpret_cast<const float4 *>(p.S + (size_t)t * p.H + r);
+    const float gs = p.gate_s[t];
+    float4 o;
+    float *op = &o.x;
+    const float *sp = &S.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float routed = wv[0] * (&yv[0].x)[c];
+#pragma unroll
+        for (int j = 1; j < kMaxTopK; ++j)
+            if (j < k) routed = fmaf(wv[j], (&yv[j].x)[c], routed);
+        float v = __fadd_rn(routed, __fmul_rn(gs, sp[c]));
+        if (p.resid) v = __fadd_rn(resid_at(p.resid, p.resid_bf16, (size_t)t * p.H + r + c), v);
+        op[c] = v;
+    }
+    *reinterpret_cast<float4 *>(p.out + (size_t)t * p.H + r) = o;
+}
+
 // ---- launchers ----------------------------------------------------------------------------
 #define MOE_ROWMAP_CASES(LAUNCH)                  \
     switch (m.lpr * 100 + m.nc) {                 \
@@ -961,6 +996,11 @@ hipError_t launch_down_join(const DownJoinParams &p, int wkind, const RowMap &m,
 }
 
 hipError_t launch_join(const JoinParams &p, hipStream_t s) {
+    const bool aligned = (((uintptr_t)p.y | (uintptr_t)p.S | (uintptr_t)p.out) & 15) == 0;
+    if (p.H % 4 == 0 && aligned) {
+        launch_kernel(k_join4, dim3((p.H + 1023) / 1024, p.T), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     const dim3 grid((p.H + 255) / 256, p.T);
     launch_kernel(k_join, grid, dim3(256), 0, s, p);
     return hipGetLastError();

@@ -4,11 +4,15 @@
 // job's weight tile is worth sharing across many tokens.  A job is 128 weight
 // rows of one expert (gate/up: 64 rows of gate and the same 64 rows of up, so
 // that silu(gate) * up is formed in registers; down: 128 rows), and a pass
-// covers 64*NTW tokens of its bucket: each of the four waves owns 16*NTW of
-// the pass's tokens and all 128 rows.  K runs in stages of 64:
+// covers 16*NW*NTW tokens of its bucket: each of the NW waves owns 16*NTW of
+// the pass's tokens and all 128 rows.  128- and 192-token passes run four waves
+// (one a SIMD, NTW 2 and 3); 256-token passes run eight waves of 32 tokens, two
+// a SIMD, whose registers fit in half the file (four waves of 64 tokens need more
+// than half, so one a SIMD, with nothing to run while it waits).  K runs in
+// stages of 64:
 //   * the weight stage (128 rows x 128 bytes) is loaded once per workgroup into
 //     LDS (double-buffered; 16-byte chunk c of row r sits at chunk position
-//     c ^ (r & 7), so the fragment reads hit distinct banks) and read by all four
+//     c ^ (r & 7), so the fragment reads hit distinct banks) and read by all the
 //     waves;
 //   * each wave loads its own token rows straight into registers; loads run two
 //     stages ahead in three register sets, and the barriers between stages order
@@ -105,10 +109,11 @@ __device__ __forceinline__ PfJob pf_decode(const GGParams &p, int j, int tb_len,
     return jb;
 }
 
-template <bool GU, int NTW>
-__global__ __launch_bounds__(256) void k_pf(GGParams p) {
+template <bool GU, int NTW, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_pf(GGParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
-    constexpr int BN = 64 * NTW;  // tokens per pass
+    constexpr int BN = 16 * NW * NTW;  // tokens per pass
+    constexpr int NQ = 16 / NW;        // 16-byte weight chunks per thread per stage
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ri = lane & 15, g = lane >> 4;
     const int T = p.T, k = p.k, npairs = T * k;
@@ -123,11 +128,11 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
         if (!jb.valid) continue;
         const size_t rb = (size_t)jb.K * 2;
         const int nst = jb.K / kPfBK;
-        // this thread's four 16-byte pieces of every weight stage: row u>>3, chunk u&7
-        const uint8_t *asrc[4];
+        // this thread's 16-byte pieces of every weight stage (NQ of them): row u>>3, chunk u&7
+        const uint8_t *asrc[NQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int u = tid + 256 * q, lr = u >> 3, ch = u & 7;
+        for (int q = 0; q < NQ; ++q) {
+            const int u = tid + 64 * NW * q, lr = u >> 3, ch = u & 7;
             const int half = lr / kHalf, r = jb.tile * kHalf + (lr - half * kHalf);
             const uint8_t *W = half ? jb.W1 : jb.W0;
             asrc[q] = W + (size_t)(r < jb.rows ? r : 0) * rb + ch * 16;
@@ -166,14 +171,14 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
 
             // three register sets in rotation: stage s is loaded two stages ahead, its
             // weights go to LDS slot s % 2 one stage ahead, its tokens feed the MFMAs
-            uint4 areg[3][4], breg[3][NTW][2];
+            uint4 areg[3][NQ], breg[3][NTW][2];
             auto load = [&](auto SI, int st) {
                 constexpr int i = decltype(SI)::value;
                 const size_t ko = (size_t)st * kPfBK * 2;
                 // unconditional (branch-free) loads: rows past the end read a clamped row,
                 // and the epilogue stores neither their rows nor their token columns
 #pragma unroll
-                for (int q = 0; q < 4; ++q) areg[i][q] = ld16(asrc[q] + ko);
+                for (int q = 0; q < NQ; ++q) areg[i][q] = ld16(asrc[q] + ko);
 #pragma unroll
                 for (int n = 0; n < NTW; ++n)
 #pragma unroll
@@ -183,8 +188,8 @@ __global__ __launch_bounds__(256) void k_pf(GGParams p) {
                 constexpr int i = decltype(SI)::value;
                 uint8_t *dst = lds + (st & 1) * kPfStage;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int u = tid + 256 * q;
+                for (int q = 0; q < NQ; ++q) {
+                    const int u = tid + 64 * NW * q;
                     *reinterpret_cast<uint4 *>(dst + (u >> 3) * kPfStride + (((u & 7) ^ ((u >> 3) & 7)) << 4)) = areg[i][q];
                 }
             };
@@ -278,7 +283,7 @@ int pf_job_count(int tiles_shared, int n_tb, int nu, int tiles_routed) {
     return pf_jobs(tiles_shared, n_tb, nu, tiles_routed);
 }
 int pf_rows_per_job(bool gate_up) { return gate_up ? kPfRows / 2 : kPfRows; }
-int pf_tokens_per_pass(int ntw) { return 64 * ntw; }
+int pf_tokens_per_pass(int ntw) { return 64 * ntw; }  // ntw 4: eight waves of 32 tokens
 
 hipError_t launch_pf(const GGParams &p, bool gate_up, int ntw, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
@@ -286,11 +291,11 @@ hipError_t launch_pf(const GGParams &p, bool gate_up, int ntw, int grid, hipStre
     if (gate_up) {
         if (ntw <= 2) launch_kernel(k_pf<true, 2>, dim3(grid), dim3(256), lds, s, p);
         else if (ntw == 3) launch_kernel(k_pf<true, 3>, dim3(grid), dim3(256), lds, s, p);
-        else launch_kernel(k_pf<true, 4>, dim3(grid), dim3(256), lds, s, p);
+        else launch_kernel(k_pf<true, 2, 8>, dim3(grid), dim3(512), lds, s, p);
     } else {
         if (ntw <= 2) launch_kernel(k_pf<false, 2>, dim3(grid), dim3(256), lds, s, p);
         else if (ntw == 3) launch_kernel(k_pf<false, 3>, dim3(grid), dim3(256), lds, s, p);
-        else launch_kernel(k_pf<false, 4>, dim3(grid), dim3(256), lds, s, p);
+        else launch_kernel(k_pf<false, 2, 8>, dim3(grid), dim3(512), lds, s, p);
     }
     return hipGetLastError();
 }
@@ -302,11 +307,11 @@ int pf_occupancy(bool gate_up, int ntw) {
     if (gate_up)
         e = ntw <= 2   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 2>, 256, lds)
             : ntw == 3 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 3>, 256, lds)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 4>, 256, lds);
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<true, 2, 8>, 512, lds);
     else
         e = ntw <= 2   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 2>, 256, lds)
             : ntw == 3 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 3>, 256, lds)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 4>, 256, lds);
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_pf<false, 2, 8>, 512, lds);
     return e == hipSuccess && n > 0 ? n : 1;
 }
 

@@ -330,10 +330,124 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     }
 }
 
+// The same GEMM for thousands of tokens, with rows split over the waves instead of K: a
+// workgroup owns 16 * NT tokens and every row (the E experts and the gate vector, in
+// 16-row tiles; wave w takes tiles w, w + 4, ..., at most RTW of them) over the whole
+// of K.  Each token row is then read once per workgroup (the four waves' loads of the
+// same token bytes meet in the L1) instead of once per 16 rows, and each weight is split
+// into its three pieces once per workgroup of 64 tokens instead of once per 16.  Each
+// logit is one accumulator over K in ascending 32-element steps.
+template <int RTW, int NT>
+__global__ __launch_bounds__(256) void k_router_mfma_rows(RouterParams p) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
+    const int ri = lane & 15, g = lane >> 4;
+    const int H = p.H, E = p.E, T = p.T;
+    const int n_tiles = (E + 1 + 15) / 16;
+    int nt = 0;  // this wave's row tiles
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) nt += wave + 4 * i < n_tiles ? 1 : 0;
+    if (nt == 0) return;
+    const float *W[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        const int row = (wave + 4 * i) * 16 + ri;  // rows past E read the gate vector, never stored
+        W[i] = (row < E ? p.router + (size_t)row * H : p.gate_vec) + 8 * g;
+    }
+    const int t0 = blockIdx.x * 16 * NT;
+    const uint16_t *xb[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int t = t0 + 16 * n + ri;
+        xb[n] = reinterpret_cast<const uint16_t *>(p.x) + (size_t)(t < T ? t : 0) * H + 8 * g;
+    }
+    rfloatx4_t acc[RTW][NT];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[i][n] = rfloatx4_t{0.f, 0.f, 0.f, 0.f};
+    struct Step {
+        float4 wa[RTW], wb[RTW];
+        uint4 b[NT];
+    };
+    const int nsteps = H / 32;
+    // loads past the last step re-read the last one and are never used; the tiles a wave
+    // does not own re-read its first tile (uniform per wave, so no divergence)
+    auto load = [&](Step &d, int s) {
+        const int ko = 32 * min(s, nsteps - 1);
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const float *w = (i < nt ? W[i] : W[0]) + ko;
+            d.wa[i] = *reinterpret_cast<const float4 *>(w);
+            d.wb[i] = *reinterpret_cast<const float4 *>(w + 4);
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) d.b[n] = ld16(xb[n] + ko);
+    };
+    auto mul = [&](const Step &d) {
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            if (i >= nt) break;
+            uint4 hi, mid, lo;
+            split3(d.wa[i], d.wb[i], hi, mid, lo);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                acc[i][n] = r_mfma(hi, d.b[n], acc[i][n]);
+                acc[i][n] = r_mfma(mid, d.b[n], acc[i][n]);
+                acc[i][n] = r_mfma(lo, d.b[n], acc[i][n]);
+            }
+        }
+    };
+    Step st[3];
+    load(st[0], 0);
+    load(st[1], 1);  // H is a multiple of 128: at least four steps
+    int s = 0;
+    for (; s + 4 < nsteps; s += 3) {
+        load(st[2], s + 2); mul(st[0]);
+        load(st[0], s + 3); mul(st[1]);
+        load(st[1], s + 4); mul(st[2]);
+    }
+    if (s + 2 < nsteps) load(st[2], s + 2);
+    mul(st[0]);
+    if (s + 1 < nsteps) { if (s + 3 < nsteps) load(st[0], s + 3); mul(st[1]); }
+    if (s + 2 < nsteps) mul(st[2]);
+    if (s + 3 < nsteps) mul(st[0]);
+    // lane holds rows 16 * tile + 4g + v for token column ri
+    const int ls = logit_stride(E);
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        if (i >= nt) break;
+        const int e0 = (wave + 4 * i) * 16 + 4 * g;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int t = t0 + 16 * n + ri;
+            if (t >= T) continue;
+            float *dst = p.logits + (size_t)t * ls + e0;
+            if (e0 + 3 <= E) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[i][n][0], acc[i][n][1], acc[i][n][2], acc[i][n][3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (e0 + v <= E) dst[v] = acc[i][n][v];
+            }
+        }
+    }
+}
+
+// row split used from this many tokens (below, the K-split kernel fills more of the GPU)
+constexpr int kRouterRowsMinTokens = 8192;
+constexpr int kRouterRowsRTW = 5, kRouterRowsNT = 4;
+
 hipError_t launch_router_mfma(const RouterParams &p, hipStream_t s) {
     if (!p.x_bf16 || p.norm_w || p.H % 128 != 0) return hipErrorInvalidValue;
     // one 16-token tile per workgroup up to 256 tokens; wider token blocks above (fewer
     // re-reads and splits of the rows)
+    const int n_tiles = (p.E + 1 + 15) / 16;
+    if (p.T >= kRouterRowsMinTokens && n_tiles > 4 * (kRouterRowsRTW - 1) && n_tiles <= 4 * kRouterRowsRTW) {
+        const int tpw = 16 * kRouterRowsNT;
+        launch_kernel(k_router_mfma_rows<kRouterRowsRTW, kRouterRowsNT>, dim3((p.T + tpw - 1) / tpw), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     const int nt = p.T <= 256 ? 1 : p.T < 4096 ? 2 : 4;
     const dim3 grid((p.E + 1 + 15) / 16, (p.T + 16 * nt - 1) / (16 * nt));
     if (nt == 1) launch_kernel(k_router_mfma<1>, grid, dim3(256), 0, s, p);

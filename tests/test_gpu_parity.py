@@ -36,8 +36,8 @@ SMALL = {
     # 512 experts: 2 tokens route in the gate/up workgroups; 12 tokens' logits rows exceed
     # what their prologue holds, so the routing launch of its own ranks them
     "bf16_512_experts": (synth.LayerShape(128, 512, 8, 64, 32, "bf16", "bf16"), 13, (2, 12)),
-    # 1 KiB rows (64-lane row mapping): 1 to 3 tokens take the gate/up jobs of one row
-    # per wave, 4 tokens those of two rows per wave
+    # 1 KiB rows (64-lane row mapping): 1 token takes the gate/up jobs of one row per
+    # wave, 2 to 4 tokens those of two rows per wave
     "bf16_kib_rows": (synth.LayerShape(512, 16, 4, 64, 32, "bf16", "bf16"), 14, (1, 2, 3, 4)),
 }
 

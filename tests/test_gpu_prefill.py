@@ -150,10 +150,12 @@ def test_repeated_runs_give_the_same_bits():
     mf.close()
 
 
-@pytest.mark.parametrize("T", [17, 512, 4096])
+@pytest.mark.parametrize("T", [17, 512, 4096, 8200])
 def test_router_logits_have_fp32_accuracy(orc, T):
     """Above 16 tokens the router is an MFMA GEMM over an exact three-way bf16 split
-    of the fp32 weights (one, two or four 16-token tiles per workgroup by the batch):
+    of the fp32 weights (one, two or four 16-token tiles per workgroup splitting K four
+    ways, and from 8192 tokens 64 tokens per workgroup over every row and all of K; 8200
+    tokens end in a partial workgroup):
     its logits must be as close to the fp64 oracle as an fp32 dot product (a plain
     bf16 rounding of the weights would be off by ~1e-3)."""
     dev = device()
