@@ -49,25 +49,68 @@ __device__ __forceinline__ float dpp_f(float v) {
 // Sum over aligned segments of LPR lanes (LPR in 8, 16, 32, 64); the result is
 // in every lane of the segment.  Each step adds a lane's value to its partner's
 // (a + b in one lane, b + a in the other), so all lanes hold identical bits.  The
-// steps across rows of 16 lanes use the gfx950 permlane swaps (no LDS round trip):
-// after a swap of a register with itself, one copy holds the lower partner's value
-// and the other the upper partner's in both lanes of every pair.
+// steps run from the widest partner distance down: halves of the wave, rows of 16
+// lanes (both with the gfx950 permlane swaps, no LDS round trip), then mirrored
+// lanes inside 16 and 8, then lane ^ 2 and lane ^ 1.  After a swap of a register with
+// itself, one copy holds the lower partner's value and the other the upper
+// partner's in both lanes of every pair, and the step adds lower + upper.
+__device__ __forceinline__ float swap32_add(float lo_keep, float hi_keep) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo_keep), __float_as_uint(hi_keep), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float swap16_add(float even_keep, float odd_keep) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(even_keep), __float_as_uint(odd_keep), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float sum_in16(float v) {
+    v = v + dpp_f<kDppMirror>(v);
+    v = v + dpp_f<kDppHalfMirror>(v);
+    v = v + dpp_f<kDppXor2>(v);
+    v = v + dpp_f<kDppXor1>(v);
+    return v;
+}
+
 template <int LPR>
 __device__ __forceinline__ float seg_sum(float v) {
     static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment size");
-    v = v + dpp_f<kDppXor1>(v);
-    v = v + dpp_f<kDppXor2>(v);
-    v = v + dpp_f<kDppHalfMirror>(v);
+    if constexpr (LPR >= 64) v = swap32_add(v, v);
+    if constexpr (LPR >= 32) v = swap16_add(v, v);
     if constexpr (LPR >= 16) v = v + dpp_f<kDppMirror>(v);
-    if constexpr (LPR >= 32) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    }
-    if constexpr (LPR >= 64) {
-        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    }
+    v = v + dpp_f<kDppHalfMirror>(v);
+    v = v + dpp_f<kDppXor2>(v);
+    v = v + dpp_f<kDppXor1>(v);
     return v;
+}
+
+// Whole-wave sums of N rows at once (N = 1, 2, 4 or 8 partial values per lane): the
+// same additions as seg_sum<64> on every row, in fewer instructions.  Each swap across
+// halves or rows of 16 takes two rows' registers, keeps one row in each half, and
+// adds, so the register count halves at every such step; the steps inside 16 lanes
+// then run on what is left.  Where the results sit: rows_lane<N>(i) is the first lane
+// holding row i (the 16-lane row or half it starts holds it in every lane), in result
+// register rows_reg<N>(i).
+template <int N> constexpr int rows_regs() { return N >= 8 ? 2 : 1; }
+template <int N> __host__ __device__ constexpr int rows_lane(int i) {
+    return N == 1 ? 0 : N == 2 ? 32 * i : N == 4 ? 16 * i : 16 * (i >> 1);
+}
+template <int N> __host__ __device__ constexpr int rows_reg(int i) { return N >= 8 ? (i & 1) : 0; }
+
+template <int N>
+__device__ __forceinline__ void seg_sum_rows(const float (&v)[N], float (&r)[rows_regs<N>()]) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "rows at once");
+    if constexpr (N == 1) {
+        r[0] = seg_sum<64>(v[0]);
+    } else if constexpr (N == 2) {  // lanes 0-31 row 0, 32-63 row 1
+        const float h = swap32_add(v[0], v[1]);
+        r[0] = sum_in16(swap16_add(h, h));
+    } else if constexpr (N == 4) {  // 16-lane row q holds row q
+        r[0] = sum_in16(swap16_add(swap32_add(v[0], v[2]), swap32_add(v[1], v[3])));
+    } else {  // register c, 16-lane row q: row c + 2q
+        const float s0 = swap32_add(v[0], v[4]), s1 = swap32_add(v[1], v[5]);
+        const float s2 = swap32_add(v[2], v[6]), s3 = swap32_add(v[3], v[7]);
+        r[0] = sum_in16(swap16_add(s0, s2));
+        r[1] = sum_in16(swap16_add(s1, s3));
+    }
 }
 
 // ---- activation functions --------------------------------------------------------

@@ -528,12 +528,35 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
                 const uint8_t *xr = lds + srow * xrow;
                 float g[RPW], u[RPW];
                 gate_up_token<WK, LPR, NC, RPW>(xr, xbias + srow * nblk, n_chunks, sl, wg, wu, sg, su, g, u);
+                if constexpr (LPR == 64 && (RPW == 1 || RPW == 2)) {
+                    // the wave's gate and up rows summed together (gate rows, then up rows),
+                    // then each row's gate sum and up sum brought into one lane
+                    constexpr int N = 2 * RPW;
+                    float pv[N], rs[1];
 #pragma unroll
-                for (int i = 0; i < RPW; ++i) {
-                    const int r = job.tile * RPWG + (wave * RPW + i) * RPI + seg;
-                    const float gs = seg_sum<LPR>(g[i]);
-                    const float us = seg_sum<LPR>(u[i]);
-                    if (sl == 0 && r < job.rows && ook) hout[(size_t)orow * hstride + r] = silu_f(gs) * us;
+                    for (int i = 0; i < RPW; ++i) {
+                        pv[i] = g[i];
+                        pv[RPW + i] = u[i];
+                    }
+                    seg_sum_rows<N>(pv, rs);
+                    // lanes holding gate row i: rows_lane<N>(i); its up row sits 32 lanes above
+                    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs[0]), __float_as_uint(rs[0]),
+                                                                    false, false);
+                    const float gs = __uint_as_float(a[0]), us = __uint_as_float(a[1]);
+#pragma unroll
+                    for (int i = 0; i < RPW; ++i) {
+                        const int r = job.tile * RPWG + wave * RPW + i;
+                        if (lane == rows_lane<N>(i) && r < job.rows && ook)
+                            hout[(size_t)orow * hstride + r] = silu_f(gs) * us;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < RPW; ++i) {
+                        const int r = job.tile * RPWG + (wave * RPW + i) * RPI + seg;
+                        const float gs = seg_sum<LPR>(g[i]);
+                        const float us = seg_sum<LPR>(u[i]);
+                        if (sl == 0 && r < job.rows && ook) hout[(size_t)orow * hstride + r] = silu_f(gs) * us;
+                    }
                 }
             }
         }
@@ -655,14 +678,26 @@ __global__ __launch_bounds__(256) void k_down(DownParams p) {
                         asum[n] += (ac.v[n][q] + ac.v[n][q + 1]) + (ac.v[n][q + 2] + ac.v[n][q + 3]);
                 }
             }
-            float v[RPW];
+            if constexpr (LPR == 64) {  // the wave's rows summed together
+                float pv[RPW], rs[rows_regs<RPW>()];
 #pragma unroll
-            for (int i = 0; i < RPW; ++i)
-                v[i] = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(ac, asum, n_chunks, sl, w, s, i));
+                for (int i = 0; i < RPW; ++i) pv[i] = down_dot<WK, LPR, NC, RPW>(ac, asum, n_chunks, sl, w, s, i);
+                seg_sum_rows<RPW>(pv, rs);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int r = job.tile * RPWG + (wave * RPW + i) * RPI + seg;
-                if (sl == 0 && r < job.rows) dst[(size_t)orow * H + r] = v[i];
+                for (int i = 0; i < RPW; ++i) {
+                    const int r = job.tile * RPWG + wave * RPW + i;
+                    if (lane == rows_lane<RPW>(i) && r < job.rows) dst[(size_t)orow * H + r] = rs[rows_reg<RPW>(i)];
+                }
+            } else {
+                float v[RPW];
+#pragma unroll
+                for (int i = 0; i < RPW; ++i)
+                    v[i] = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(ac, asum, n_chunks, sl, w, s, i));
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const int r = job.tile * RPWG + (wave * RPW + i) * RPI + seg;
+                    if (sl == 0 && r < job.rows) dst[(size_t)orow * H + r] = v[i];
+                }
             }
         }
     };
@@ -797,10 +832,20 @@ __global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
                     asum[n] += (U.ac.v[n][q] + U.ac.v[n][q + 1]) + (U.ac.v[n][q + 2] + U.ac.v[n][q + 3]);
             }
         }
+        if constexpr (LPR == 64) {  // the unit's rows summed together
+            float pv[RPW], rs[rows_regs<RPW>()];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const float v = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(U.ac, asum, U.nch, sl, U.w, U.sc, i));
-            if (sl == 0 && U.ok) s_y[U.slot * RT + i * RPI + seg] = v;
+            for (int i = 0; i < RPW; ++i) pv[i] = down_dot<WK, LPR, NC, RPW>(U.ac, asum, U.nch, sl, U.w, U.sc, i);
+            seg_sum_rows<RPW>(pv, rs);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+                if (lane == rows_lane<RPW>(i) && U.ok) s_y[U.slot * RT + i] = rs[rows_reg<RPW>(i)];
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                const float v = seg_sum<LPR>(down_dot<WK, LPR, NC, RPW>(U.ac, asum, U.nch, sl, U.w, U.sc, i));
+                if (sl == 0 && U.ok) s_y[U.slot * RT + i * RPI + seg] = v;
+            }
         }
     };
     // units in turn per wave, two register sets ping-ponging where a unit's registers are

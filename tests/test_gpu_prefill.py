@@ -37,8 +37,9 @@ SMALL = {
     # the prefill GEMM's 192- and 256-token passes with its pipelined K loop running (it
     # needs at least 5 stages of 64: K >= 320 in gate/up (K = hidden 512) and in down
     # (K = inter 384)): mean buckets of 100 (192-token passes), 200 and 300 (256-token
-    # passes; at 300 most buckets take a second, partial pass)
-    "bf16_prefill_passes": (synth.LayerShape(512, 8, 2, 384, 384, "bf16", "bf16"), 50, (400, 800, 1200), 0),
+    # passes; at 300 most buckets take a second, partial pass), and 525 (two or three
+    # 256-token passes a bucket)
+    "bf16_prefill_passes": (synth.LayerShape(512, 8, 2, 384, 384, "bf16", "bf16"), 50, (400, 800, 1200, 2100), 0),
 }
 
 
