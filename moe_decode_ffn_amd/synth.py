@@ -81,6 +81,7 @@ WORKLOADS = {
     "decode_bf16_t1": (DECODE_BF16, 1, (1,)),
     "decode_bf16_t8": (DECODE_BF16, 2, (8,)),
     "decode_q4_t1_t4": (DECODE_Q4, 3, (1, 4)),
+    "decode_q4_t1": (DECODE_Q4, 3, (1,)),
     "decode_bf16_t128": (DECODE_BF16, 4, (128,)),
     # prefill chunks: every expert busy, ~128 and ~512 tokens per expert
     "prefill_bf16_t4096": (DECODE_BF16, 5, (4096,)),

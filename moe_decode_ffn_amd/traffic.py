@@ -13,6 +13,12 @@ here launches a kernel of the layer):
         Per-dispatch means of the shader counters found under the directories (SQ_*),
         with instructions per wave and the share of wave cycles issuing or waiting.
 
+    python -m moe_decode_ffn_amd.traffic kernels --dir DIR --title TEXT --command CMD \\
+        --bench-json FILE --out profiles/kernels_<workload>.md
+        The per-kernel table of a `rocprofv3 --kernel-trace --stats` run (calls, average,
+        minimum and maximum duration), with the kernel source hash and the step time and
+        used-expert count bench.py printed under the profiler.
+
     python -m moe_decode_ffn_amd.traffic summarize --fetch DIR --write DIR \\
         --cal-fetch DIR --cal-write DIR --cal-mib N --kernel REGEX \\
         --workload NAME --shared-mode MODE --kernel-id ID --out profiles/traffic_<workload>.md
@@ -192,6 +198,51 @@ def cmd_counters(args) -> int:
     return 0
 
 
+def cmd_kernels(args) -> int:
+    """Kernel table of a rocprofv3 --stats run (its kernel_stats.csv)."""
+    files = glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows = [r for r in rows if "moeffn::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    bench = {}
+    if args.bench_json and os.path.exists(args.bench_json):
+        with open(args.bench_json) as fh:
+            for ln in fh:
+                if ln.strip().startswith("{"):
+                    bench = __import__("json").loads(ln)
+    mode = bench.get("config", {}).get("shared_mode", "?")
+    lines = [f"# Kernel trace: {args.title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", args.command, "```", "",
+             f"Kernel source hash: `{kernel_source_hash()}`; shared-expert mode: {mode}.",
+             "Calls include warm-up, the timed steps and the event-timed pass of bench.py.", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    tot = 0.0
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("moeffn::", "")
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{name}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+        tot += avg
+    lines += ["", f"Sum of per-launch averages: {tot:.2f} us (a kernel launched more than once per step, "
+                  "or not every step, counts once here)."]
+    if bench:
+        lines.append(f"bench.py under the profiler: {bench['ms_per_step'] * 1e3:.2f} us/step, "
+                     f"{bench.get('unique_experts_per_step', 0):.1f} used experts per step.")
+    lines += ["(The profiler adds dispatch overhead per launch to the step time, and its own signals to",
+              "every dispatch, so the HIP-event kernel times bench.py prints under it are inflated; the",
+              "durations above are the profiler's own.  Run without the profiler, bench.py times each",
+              "kernel with HIP events in its dispatch; those are what its roofline uses.)", ""]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def read_summary(path: str) -> dict | None:
     """The fenced `traffic` block of a summary written by summarize, or None."""
     if not os.path.exists(path):
@@ -223,6 +274,12 @@ def main(argv=None) -> int:
                    help="the profiling id of the kernel (moe_ffn_kernel_id name, e.g. gate_up, gg_gate_up)")
     s.add_argument("--extra", action="append")
     s.add_argument("--command", action="append", help="a command line to record in the summary")
+    kt = sub.add_parser("kernels")
+    kt.add_argument("--dir", required=True)
+    kt.add_argument("--title", required=True)
+    kt.add_argument("--command", required=True)
+    kt.add_argument("--bench-json", default=None)
+    kt.add_argument("--out", required=True)
     k = sub.add_parser("counters")
     k.add_argument("--dir", action="append", required=True)
     k.add_argument("--kernel", required=True)
@@ -230,7 +287,8 @@ def main(argv=None) -> int:
     k.add_argument("--out", required=True)
     k.add_argument("--command", action="append")
     args = ap.parse_args(argv)
-    return {"copy": cmd_copy, "summarize": cmd_summarize, "counters": cmd_counters}[args.cmd](args)
+    return {"copy": cmd_copy, "summarize": cmd_summarize, "counters": cmd_counters,
+            "kernels": cmd_kernels}[args.cmd](args)
 
 
 if __name__ == "__main__":
