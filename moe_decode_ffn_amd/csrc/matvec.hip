@@ -890,34 +890,12 @@ __global__ __launch_bounds__(64 * kDJWaves) void k_down_join(DownJoinParams p) {
 }
 
 // ---- join ---------------------------------------------------------------------------------
+// out = sum_j w_j y_j + s * S, four columns a thread (hidden sizes are multiples of 32 and
+// every tensor is 16-byte aligned): 16-byte loads and stores, one workgroup per 1024
+// columns of a token, every load issued before the first use (one memory round trip, not
+// k); per column, the products and sums in slot order, the gate product and the final add
+// rounded separately.
 __global__ __launch_bounds__(256) void k_join(JoinParams p) {
-    const int t = blockIdx.y;
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= p.H) return;
-    const int k = p.k;
-    const float *wt = p.wts + (size_t)t * k;
-    const float *yr = p.y + (size_t)t * k * p.H + r;
-    // issue every load before the first use (one memory round trip, not k)
-    float yv[kMaxTopK], wv[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        yv[j] = j < k ? yr[(size_t)j * p.H] : 0.f;
-        wv[j] = j < k ? wt[j] : 0.f;
-    }
-    const float S = p.S[(size_t)t * p.H + r];
-    float routed = wv[0] * yv[0];
-#pragma unroll
-    for (int j = 1; j < kMaxTopK; ++j)
-        if (j < k) routed = fmaf(wv[j], yv[j], routed);
-    float o = __fadd_rn(routed, __fmul_rn(p.gate_s[t], S));
-    if (p.resid) o = __fadd_rn(resid_at(p.resid, p.resid_bf16, (size_t)t * p.H + r), o);
-    p.out[(size_t)t * p.H + r] = o;
-}
-
-// The same join four columns a thread (hidden sizes that are a multiple of 4): 16-byte
-// loads and stores, one workgroup per 1024 columns of a token; each column's arithmetic
-// is k_join's, in the same order.
-__global__ __launch_bounds__(256) void k_join4(JoinParams p) {
     const int t = blockIdx.y;
     const int r = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (r >= p.H) return;
@@ -1042,12 +1020,8 @@ hipError_t launch_down_join(const DownJoinParams &p, int wkind, const RowMap &m,
 
 hipError_t launch_join(const JoinParams &p, hipStream_t s) {
     const bool aligned = (((uintptr_t)p.y | (uintptr_t)p.S | (uintptr_t)p.out) & 15) == 0;
-    if (p.H % 4 == 0 && aligned) {
-        launch_kernel(k_join4, dim3((p.H + 1023) / 1024, p.T), dim3(256), 0, s, p);
-        return hipGetLastError();
-    }
-    const dim3 grid((p.H + 255) / 256, p.T);
-    launch_kernel(k_join, grid, dim3(256), 0, s, p);
+    if (p.H % 4 != 0 || !aligned) return hipErrorInvalidValue;  // the plan and the forward rule these out
+    launch_kernel(k_join, dim3((p.H + 1023) / 1024, p.T), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
