@@ -34,12 +34,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // ---- cross-lane ---------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
 // quad_perm [3,2,1,0] (lane ^ 3), row_half_mirror (reverse within 8 lanes),
-// row_mirror (reverse within 16).
+// row_mirror (reverse within 16), row_ror:8 (rotate a row of 16 by 8: lane ^ 8).
 constexpr int kDppXor1 = 0xb1;
 constexpr int kDppXor2 = 0x4e;
 constexpr int kDppRevQuad = 0x1b;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRowRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

@@ -19,30 +19,25 @@ namespace moeffn {
 constexpr int kRouterWaves = 4;
 constexpr int kRouterTile = 8;  // most tokens per workgroup column
 
-// Sums eight values across each aligned segment of LPR lanes (LPR in 8..64) in
-// one transposed butterfly: three halving exchanges leave every lane holding a
-// partial sum of one token (tok = the lane's bits LPR/2, LPR/4, LPR/8), and the
-// LPR/8 lanes that share a token finish the sum; all of them hold identical bits.
-template <int LPR>
-__device__ __forceinline__ float seg_sum8(const float (&a)[8], int sl, int &tok) {
-    constexpr int d1 = LPR / 2, d2 = LPR / 4, d3 = LPR / 8;
-    const bool h1 = (sl & d1) != 0, h2 = (sl & d2) != 0, h3 = (sl & d3) != 0;
-    float b[4], c[2];
+// Sums eight values over the wave in one transposed butterfly: each exchange keeps
+// half of the values in each half of its lane group and adds the partner's copy, so
+// after the swaps across halves (permlane32), across rows of 16 (permlane16) and across
+// the two 8-lane halves of a row (a row rotation by 8) every lane holds a partial sum of
+// one value, tok = lane bits 32, 16, 8 read as 4, 2, 1; the 8 lanes that share tok then
+// finish the sum inside their group.  Each step adds two partial sums that are the same
+// in both lanes of a pair, so all 8 lanes end with identical bits.
+__device__ __forceinline__ float seg_sum8(const float (&a)[8], int lane, int &tok) {
+    const bool h3 = (lane & 8) != 0;
+    float b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float send = h1 ? a[i] : a[i + 4], keep = h1 ? a[i + 4] : a[i];
-        b[i] = keep + __shfl_xor(send, d1);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float send = h2 ? b[i] : b[i + 2], keep = h2 ? b[i + 2] : b[i];
-        c[i] = keep + __shfl_xor(send, d2);
-    }
-    const float send = h3 ? c[0] : c[1], keep = h3 ? c[1] : c[0];
-    float v = keep + __shfl_xor(send, d3);
-#pragma unroll
-    for (int m = d3 / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    tok = (h1 ? 4 : 0) + (h2 ? 2 : 0) + (h3 ? 1 : 0);
+    for (int i = 0; i < 4; ++i) b[i] = swap32_add(a[i], a[i + 4]);        // halves keep i / i + 4
+    const float c0 = swap16_add(b[0], b[2]), c1 = swap16_add(b[1], b[3]);  // rows keep 0 / 2
+    const float send = h3 ? c0 : c1, keep = h3 ? c1 : c0;
+    float v = keep + dpp_f<kDppRowRor8>(send);
+    v = v + dpp_f<kDppHalfMirror>(v);
+    v = v + dpp_f<kDppXor2>(v);
+    v = v + dpp_f<kDppXor1>(v);
+    tok = ((lane & 32) ? 4 : 0) + ((lane & 16) ? 2 : 0) + (h3 ? 1 : 0);
     return v;
 }
 
@@ -149,8 +144,8 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
         }
     }
     int tok = 0;
-    const float sum = seg_sum8<64>(acc, lane, tok);
-    const float sq = norm ? seg_sum8<64>(ss, lane, tok) : 0.f;
+    const float sum = seg_sum8(acc, lane, tok);
+    const float sq = norm ? seg_sum8(ss, lane, tok) : 0.f;
     if ((lane & 7) == 0) {
         s_part[wave][0][tok] = sum;
         s_part[wave][1][tok] = sq;
