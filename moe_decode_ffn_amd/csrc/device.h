@@ -34,13 +34,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // ---- cross-lane ---------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
 // quad_perm [3,2,1,0] (lane ^ 3), row_half_mirror (reverse within 8 lanes),
-// row_mirror (reverse within 16), row_ror:8 (rotate a row of 16 by 8: lane ^ 8).
+// row_mirror (reverse within 16), row_ror:8 (rotate a row of 16 by 8: lane ^ 8),
+// row_shr:n (lane i of a row reads lane i - n of the same row).
 constexpr int kDppXor1 = 0xb1;
 constexpr int kDppXor2 = 0x4e;
 constexpr int kDppRevQuad = 0x1b;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -81,6 +83,21 @@ __device__ __forceinline__ float seg_sum(float v) {
     v = v + dpp_f<kDppXor2>(v);
     v = v + dpp_f<kDppXor1>(v);
     return v;
+}
+
+// Inclusive prefix sum of an integer over the 64 lanes of a wave (every lane active):
+// shifts of 1, 2, 4 and 8 lanes inside each row of 16 (DPP row shifts; a lane with no
+// source lane adds 0), then each row adds the totals of the rows below it, read from
+// their last lanes.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true);
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Whole-wave sums of N rows at once (N = 1, 2, 4 or 8 partial values per lane): the

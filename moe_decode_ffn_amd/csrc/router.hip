@@ -516,11 +516,7 @@ __global__ __launch_bounds__(256) void k_count_scan(RouterParams p, int W) {
     int a = 0;
     for (int i = 0; i < per; ++i)
         if (w0 + i < W) a += col[(size_t)(w0 + i) * E];
-    int ia = a;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(ia, d);
-        if (lane >= d) ia += y;
-    }
+    const int ia = wave_incl_scan(a, lane);
     if (lane == 63) s_wsum[wave] = ia;
     __syncthreads();
     int base = ia - a;
@@ -550,11 +546,7 @@ __global__ __launch_bounds__(256) void k_bucket_batch(RouterParams p) {
     const int e0 = 2 * tid;
     const int c0 = e0 < E ? cnt[e0] : 0, c1 = e0 + 1 < E ? cnt[e0 + 1] : 0;
     int a = c0 + c1, b = (c0 > 0) + (c1 > 0);
-    int ia = a, ib = b;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int ya = __shfl_up(ia, d), yb = __shfl_up(ib, d);
-        if (lane >= d) { ia += ya; ib += yb; }
-    }
+    const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
     if (lane == 63) { s_wsum[0][wave] = ia; s_wsum[1][wave] = ib; }
     __syncthreads();
     int ba = ia - a, bb = ib - b;

@@ -313,11 +313,7 @@ __device__ void bucket_pairs(const int *ids, int T, int k, int E, uint32_t *scra
         const int e = tid * EPT + i;
         if (e < E) { a += cnt[e]; b += cnt[e] > 0; }
     }
-    int ia = a, ib = b;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int ya = __shfl_up(ia, d), yb = __shfl_up(ib, d);
-        if (lane >= d) { ia += ya; ib += yb; }
-    }
+    const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
     if (lane == 63) { wtot[wave] = ia; wtot[16 + wave] = ib; }
     lds_barrier();
     int ba = ia - a;
