@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
         nu = nu < 0 ? 0 : nu > p.E ? p.E : nu;
         if (j >= p.tiles_shared + nu * p.tiles_routed) return;
     }
-    if (!route_here || j < p.tiles_shared) {  // a shared-expert job needs no routing
+    if (!route_here) {
         ja = decode(j);
         load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
         loaded = true;
@@ -418,9 +418,13 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
             publish(0, need + 1);
             lds_barrier();
             nu = k;
-            if (need >= 0) {
+            // a first job of the shared expert issues its loads here too, not before the
+            // routing: with one load site for the first job the compiler keeps one register
+            // set for it, where two sites made it copy the set at their merge and so wait
+            // for the loads in flight there, before the rest of the routing
+            if (need >= 0 || j < p.tiles_shared) {
                 ja = decode(j);
-                early_e = lslots[need].x;
+                if (need >= 0) early_e = lslots[need].x;
                 load_rows<WK, LPR, NC, RPW, true>(ja, wave, seg, sl, ag, au, asg, asu, p.swg, p.ssg);
                 loaded = true;
             }
