@@ -291,7 +291,10 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPR, sl = lane % LPR;
-    const int H = p.H, T = p.T, k = p.k;
+    // the one-row variant serves a single token only (gate_up_one_row): a compile-time T = 1
+    // drops the batch paths (other tokens, bucketing) from it, and the scalar registers they
+    // held no longer spill
+    const int H = p.H, T = RPWX == 1 ? 1 : p.T, k = p.k;
     const int n_chunks = (int)(row_bytes<WK>(H) / 16);
     const int npairs = T * k;
     const size_t xrow = (size_t)H * XB;
