@@ -282,7 +282,8 @@ __host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int s
 // that every record read has one known address space (a read through a pointer that
 // may point to either is a flat load, which makes every later wait a wait for all
 // outstanding memory operations).
-template <int WK, int LPR, int NC, bool RH, int RPWX = 0>
+// ONE: the launch serves a single token (the one-row variant always does).
+template <int WK, int LPR, int NC, bool RH, int RPWX = 0, bool ONE = (RPWX == 1)>
 __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     constexpr int RPW = RPWX ? RPWX : WTraits<WK>::rpw_gu;  // rows per wave per job
     constexpr int RPI = 64 / LPR;
@@ -291,10 +292,10 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPR, sl = lane % LPR;
-    // the one-row variant serves a single token only (gate_up_one_row): a compile-time T = 1
-    // drops the batch paths (other tokens, bucketing) from it, and the scalar registers they
-    // held no longer spill
-    const int H = p.H, T = RPWX == 1 ? 1 : p.T, k = p.k;
+    // a single-token instance (the one-row variant, and 4-bit rows routed here at batch 1)
+    // has T = 1 at compile time: the batch paths (other tokens, bucketing) drop out, and
+    // the scalar registers they held no longer spill
+    const int H = p.H, T = ONE ? 1 : p.T, k = p.k;
     const int n_chunks = (int)(row_bytes<WK>(H) / 16);
     const int npairs = T * k;
     const size_t xrow = (size_t)H * XB;
@@ -977,6 +978,12 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
 #undef GU_ONE_ROW
         return hipGetLastError();
     }
+#define GU_Q4_ONE(L, N) launch_kernel(k_gate_up<W_Q4, L, N, true, 0, true>, dim3(grid), dim3(256), lds, s, p);
+    if (rh && p.T == 1 && wkind == W_Q4) {  // 4-bit rows, one token routed in the workgroups
+        MOE_ROWMAP_CASES(GU_Q4_ONE)
+        return hipGetLastError();
+    }
+#undef GU_Q4_ONE
 #define GU_LAUNCH_RH(L, N, RH)                                                                               \
     if (wkind == W_F32) launch_kernel(k_gate_up<W_F32, L, N, RH>, dim3(grid), dim3(256), lds, s, p);         \
     else if (wkind == W_BF16) launch_kernel(k_gate_up<W_BF16, L, N, RH>, dim3(grid), dim3(256), lds, s, p);  \
