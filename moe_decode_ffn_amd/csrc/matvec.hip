@@ -282,8 +282,9 @@ __host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int s
 // that every record read has one known address space (a read through a pointer that
 // may point to either is a flat load, which makes every later wait a wait for all
 // outstanding memory operations).
-// ONE: the launch serves a single token (the one-row variant always does).
-template <int WK, int LPR, int NC, bool RH, int RPWX = 0, bool ONE = (RPWX == 1)>
+// ONE: the launch serves a single token (the one-row variant always does).  SMALL: it
+// serves 2 or more tokens with at most 64 (token, slot) pairs, which one wave buckets.
+template <int WK, int LPR, int NC, bool RH, int RPWX = 0, bool ONE = (RPWX == 1), bool SMALL = false>
 __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     constexpr int RPW = RPWX ? RPWX : WTraits<WK>::rpw_gu;  // rows per wave per job
     constexpr int RPI = 64 / LPR;
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
             // the other tokens (wave w takes tokens w, w + 4, ...; token 0 is done), then the
             // bucketing, whose first barrier orders every wave's picks
             rank_tokens(lgt, 1, T, p.E, k, area, L, g);
-            nu = bucket_tokens(T, k, p.E, area, L, g);
+            nu = bucket_tokens<SMALL>(T, k, p.E, area, L, g);
             if (need >= 0) {
                 // the job's tokens: its bucket as finished (the same expert)
                 const int4 sv = lslots[need];
@@ -978,6 +979,12 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
 #undef GU_ONE_ROW
         return hipGetLastError();
     }
+#define GU_BF16_SMALL(L, N) launch_kernel(k_gate_up<W_BF16, L, N, true, 0, false, true>, dim3(grid), dim3(256), lds, s, p);
+    if (rh && p.T > 1 && p.T * p.k <= 64 && wkind == W_BF16) {  // bf16, 2-8 tokens of top-8
+        MOE_ROWMAP_CASES(GU_BF16_SMALL)
+        return hipGetLastError();
+    }
+#undef GU_BF16_SMALL
 #define GU_Q4_ONE(L, N) launch_kernel(k_gate_up<W_Q4, L, N, true, 0, true>, dim3(grid), dim3(256), lds, s, p);
     if (rh && p.T == 1 && wkind == W_Q4) {  // 4-bit rows, one token routed in the workgroups
         MOE_ROWMAP_CASES(GU_Q4_ONE)

@@ -426,6 +426,8 @@ __device__ inline void rank_tokens(const float *logits, int t_lo, int t_hi, int 
 // builds the job records in g.records and copies the tables to g where its
 // pointers are set.  Barriers inside: call from every thread of the workgroup.
 // Returns the used-expert count.
+// WAVE_ONLY: the caller guarantees T * k <= 64 (the workgroup bucketing is left out).
+template <bool WAVE_ONLY = false>
 __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const RouteLds &L,
                                     const RouteGlobal &g) {
     const int tid = threadIdx.x, NP = T * k;
@@ -446,7 +448,7 @@ __device__ inline int bucket_tokens(int T, int k, int E, uint8_t *area, const Ro
             }
             if (j == 0) *nup = k;
         }
-    } else if (NP <= 64) {  // one wave sorts the pairs (no barrier inside)
+    } else if (WAVE_ONLY || NP <= 64) {  // one wave sorts the pairs (no barrier inside)
         if (threadIdx.x < 64) bucket_pairs_wave(ids, NP, E, slots, pairs, pose, nup);
     } else {
         bucket_pairs(ids, T, k, E, reinterpret_cast<uint32_t *>(area + L.scratch), slots, pairs, pose, nup);
