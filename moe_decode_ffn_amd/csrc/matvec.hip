@@ -277,6 +277,21 @@ __host__ __device__ inline size_t stage_bytes(int toks, int H, int xbytes, int s
     return stage_x_bytes(toks, H, xbytes) + (sums ? (((size_t)toks * (H / 32) * 4 + 15) & ~(size_t)15) : 0);
 }
 
+// Prefetch loads per thread (256 threads) for one token's row: a row of n chunks maps to
+// LPR * NC >= n chunks of weights, and the token row is as many 16-byte chunks (4x for
+// 4-bit rows, whose 32 elements take one chunk against four of bf16 tokens).  One token's
+// logits row is at most 129 chunks (512 experts).
+__host__ __device__ constexpr int one_token_x_loads(int wk, int lpr, int nc) {
+    return ((wk == W_Q4 ? 4 : 1) * lpr * nc + 255) / 256 < 1 ? 1
+           : ((wk == W_Q4 ? 4 : 1) * lpr * nc + 255) / 256 > 8 ? 8
+                                                               : ((wk == W_Q4 ? 4 : 1) * lpr * nc + 255) / 256;
+}
+__host__ inline bool one_token_stage_fits(const GateUpParams &p, int wkind, const RowMap &m) {
+    const size_t xb = wkind == W_F32 ? 4 : 2;
+    return (size_t)p.H * xb / 16 <= 256 * (size_t)one_token_x_loads(wkind, m.lpr, m.nc) &&
+           logit_stride(p.E) / 4 <= 256;
+}
+
 // RH: the workgroups rank and bucket the batch themselves (the job records then live
 // in LDS; else in memory, written by a routing launch).  A compile-time choice, so
 // that every record read has one known address space (a read through a pointer that
@@ -343,7 +358,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     // reach LDS together before the routing, so that nothing between the bucketing and the
     // first computation waits for a load (a barrier that also waited for memory would hold
     // back the first job's weight loads and, behind them, the second job's).
-    constexpr int kLgPre = 5, kXPre = 8;
+    // a single-token instance loads only what one token can need (one_token_x_loads)
+    constexpr int kLgPre = ONE ? 1 : 5, kXPre = ONE ? one_token_x_loads(WK, LPR, NC) : 8;
     const int n16lg = route_here ? T * logit_stride(p.E) / 4 : 0;
     uint4 lgpre[kLgPre];
     load_chunks<kLgPre>(lgpre, n16lg, tid, [&](int i) { return reinterpret_cast<const uint8_t *>(p.logits) + 16 * (size_t)i; });
@@ -966,6 +982,9 @@ hipError_t launch_gate_up(const GateUpParams &p, int wkind, const RowMap &m, int
     const size_t lds = gate_up_lds_bytes(p, wkind == W_F32 ? 4 : 2);
     if (lds > kLdsLimit) return hipErrorInvalidValue;
     const bool rh = p.routed && p.route_here;
+    if ((gate_up_one_row(wkind, m, p.T, rh) || (rh && p.T == 1 && wkind == W_Q4)) &&
+        !one_token_stage_fits(p, wkind, m))
+        return hipErrorInvalidValue;  // cannot happen: the row map covers the token row
     if (gate_up_one_row(wkind, m, p.T, rh)) {
 #define GU_ONE_ROW(L, N) launch_kernel(k_gate_up<W_BF16, 64, N, true, 1>, dim3(grid), dim3(256), lds, s, p);
         switch (m.nc) {
