@@ -91,13 +91,20 @@ __global__ __launch_bounds__(256) void k_router(RouterParams p) {
     const int xrow = H * (XBF ? 2 : 4);
     const uint8_t *xs = (const uint8_t *)p.x + (size_t)t0 * xrow;
     {
-        // the tile is at most kStageBytes: 8 chunks per thread
+        // the tile is at most kStageBytes: 8 chunks per thread; a tile of at most one chunk
+        // per thread (a single token of up to 2048 bf16 elements) issues one load, not eight
+        // (a branch on a value all threads of the workgroup share)
         const int n16 = nt * xrow / 16;
-        uint4 xv[8];
-        load_chunks<8>(xv, n16, tid, [&](int i) { return xs + 16 * (size_t)i; });
+        auto stage = [&](auto NQ) {
+            constexpr int Q = decltype(NQ)::value;
+            uint4 xv[Q];
+            load_chunks<Q>(xv, n16, tid, [&](int i) { return xs + 16 * (size_t)i; });
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (tid + 256 * q < n16) reinterpret_cast<uint4 *>(lds)[tid + 256 * q] = xv[q];
+            for (int q = 0; q < Q; ++q)
+                if (tid + 256 * q < n16) reinterpret_cast<uint4 *>(lds)[tid + 256 * q] = xv[q];
+        };
+        if (n16 <= 256) stage(std::integral_constant<int, 1>{});
+        else stage(std::integral_constant<int, 8>{});
     }
     __syncthreads();
     if (norm) {
