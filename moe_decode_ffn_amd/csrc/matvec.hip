@@ -315,6 +315,13 @@ __global__ __launch_bounds__(256) void k_gate_up(GateUpParams p) {
     const int n_chunks = (int)(row_bytes<WK>(H) / 16);
     const int npairs = T * k;
     const size_t xrow = (size_t)H * XB;
+    if constexpr (ONE || SMALL) {
+        // the arguments a job's decode reads, fetched with the kernel's first scalar loads
+        // rather than where the first job is decoded, after the routing barrier (measured
+        // faster for batches of 1-8 tokens, slower for the general instances at 16)
+        asm volatile("" ::"s"(p.wg), "s"(p.wu), "s"(p.I), "s"(p.swg), "s"(p.swu), "s"(p.Is));
+        if constexpr (WK == W_Q4) asm volatile("" ::"s"(p.sg), "s"(p.su), "s"(p.ssg), "s"(p.ssu));
+    }
     // 4-bit rows: each block's activation bias, after the staged tokens
     float *xbias = reinterpret_cast<float *>(lds + stage_x_bytes(p.x_resident ? T : p.tok_per_pass, H, XB));
     const int nblk = H / 32;
